@@ -1,0 +1,16 @@
+"""CPU oracle (float64 NumPy) for causal softmax attention and the
+Nadaraya-Watson control.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``, never by the library.  It shares
+no code with the GPU path.
+
+Parity pins (what ties each function to something other than itself) live in
+``tests/test_oracle_*.py``.  No function here is "parity unpinned".
+"""
+from .attention import (DEFAULT_SCALE, backward, backward_head, forward, forward_head,
+                        forward_head_relational, loss)
+from .nw import nw_average
+
+__all__ = ["DEFAULT_SCALE", "forward", "forward_head", "forward_head_relational", "backward",
+           "backward_head", "loss", "nw_average"]

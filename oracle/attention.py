@@ -1,0 +1,216 @@
+"""Oracle for causal softmax attention: the naive plan, in float64, on the CPU.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  It shares
+no code with the GPU library and never imports it.
+
+What it computes follows "Show HN: automatic deduction of FlashAttention kernel
+from 25 lines of SQL" (neshdevtech.com), the view ``attention`` in its two SQL
+spellings (``ATTENTION_WINDOW`` and ``ATTENTION_GROUP_BY``), the loss of the
+``GRADIENT`` statement and the JAX ``attention()``/``loss()`` functions:
+
+* scores   s_ij = (sum_d q_id k_jd) / 8   for every pair with i >= j (the join
+  predicate ``q.t >= k.t``; pairs with j > i do not exist);
+* m_i      = max_j s_ij over the pairs that exist (a window, or a GROUP BY);
+* w_ij     = exp(s_ij - m_i);   z_i = sum_j w_ij;
+* o_id     = sum_j (w_ij / z_i) v_jd, summed over existing pairs only, so an
+  absent pair never contributes 0 * v (an infinity in V reaches only rows
+  i >= j);
+* loss     = sum(o^2) / 2, so the upstream gradient is dO = O;
+* lse_i    = m_i + ln z_i (natural log of the scaled scores).  The pages do not
+  name this quantity; it is the per-row value a streamed backward needs.
+
+The scale is an argument; the pages fix it at 1/8 (= 1/sqrt(64)).  Dividing by
+8 and multiplying by 0.125 give the same float64 result, since 0.125 is a power
+of two.
+
+The backward pages use ddx and ``jax.grad`` and do not print an algorithm.  The
+oracle takes the closed-form chain rule through the same definitions:
+
+* P = w / z,  dV_j = sum_{i>=j} P_ij dO_i,  dP_ij = dO_i . v_j,
+* delta_i = sum_j P_ij dP_ij,  dS_ij = P_ij (dP_ij - delta_i),
+* dQ_i = scale * sum_{j<=i} dS_ij k_j,  dK_j = scale * sum_{i>=j} dS_ij q_i.
+
+The row max is a constant to this derivative: it cancels from w / z, so its own
+gradient sums to zero (the page's comment above ``ATTENTION_WINDOW``).  With
+``route_max=True`` the backward also adds the term that flows through the max
+to the argmax pair, as an autodiff of the window would, which must change
+nothing beyond rounding.
+
+Rows are processed in blocks of ``block`` queries only to bound memory: every
+row's whole score vector is materialised and reduced exactly (two passes: max,
+then exp and sum).  No running (online) softmax appears here.
+"""
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+DEFAULT_SCALE = 0.125
+
+
+def _present(r0: int, r1: int, ncols: int) -> np.ndarray:
+    """Boolean (r1-r0, ncols) table of the pairs that exist: key j <= query i."""
+    i = np.arange(r0, r1)[:, None]
+    j = np.arange(ncols)[None, :]
+    return j <= i
+
+
+def _sum_present(weights: np.ndarray, present: np.ndarray, values: np.ndarray) -> np.ndarray:
+    """sum_j weights[i, j] * values[j, :] over the pairs that exist.
+
+    An absent pair contributes nothing (not 0 * v): finite values go through
+    one product with absent weights set to 0, and each non-finite value is
+    added only to the rows whose pair with it exists.  A present pair whose
+    weight underflowed to 0 still multiplies, as the SQL engine would."""
+    finite = np.isfinite(values)
+    out = np.where(present, weights, 0.0) @ np.where(finite, values, 0.0)
+    for j, d in zip(*np.nonzero(~finite)):
+        with np.errstate(invalid="ignore"):
+            term = weights[:, j] * values[j, d]
+        out[:, d] += np.where(present[:, j], term, 0.0)
+    return out
+
+
+def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                 scale: float = DEFAULT_SCALE, block: int = 256):
+    """Window spelling, matrix form.  q, k, v: (N, D) float64.
+
+    Returns (o, lse, m, z): o (N, D), and per-row lse, max m, denominator z."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    n = q.shape[0]
+    o = np.empty_like(q)
+    lse = np.empty(n)
+    m_all = np.empty(n)
+    z_all = np.empty(n)
+    for r0 in range(0, n, block):
+        r1 = min(n, r0 + block)
+        present = _present(r0, r1, r1)
+        s = (q[r0:r1] @ k[:r1].T) * scale                       # scores
+        m = np.max(np.where(present, s, -np.inf), axis=1)       # MAX(s) OVER (PARTITION BY i)
+        with np.errstate(invalid="ignore", over="ignore"):
+            w = np.where(present, np.exp(s - m[:, None]), 0.0)  # exp(s - max)
+        z = w.sum(axis=1)                                       # SUM(w) GROUP BY i
+        o[r0:r1] = _sum_present(w / z[:, None], present, v[:r1])  # SUM(w / z * v)
+        lse[r0:r1] = m + np.log(z)
+        m_all[r0:r1] = m
+        z_all[r0:r1] = z
+    return o, lse, m_all, z_all
+
+
+def forward_head_relational(q: np.ndarray, k: np.ndarray, v: np.ndarray,
+                            scale: float = DEFAULT_SCALE, spelling: str = "group by"):
+    """The view as relations in long format, one row per existing (i, j) pair.
+
+    ``spelling="group by"`` computes each row's max as a GROUP BY and joins it
+    back to the pairs; ``"window"`` takes the max over each pair's partition by
+    sorting the pair rows by i.  Aggregates are scatter-adds over the pair
+    rows, so absent pairs are never touched.  Quadratic memory: small N only.
+    Returns (o, lse)."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    n, d = q.shape
+    ii, jj = np.nonzero(np.tril(np.ones((n, n), dtype=bool)))   # q JOIN k WHERE q.t >= k.t
+    s = np.einsum("pd,pd->p", q[ii], k[jj]) * scale               # SUM(q.x * k.x) GROUP BY q.t, k.t
+    if spelling == "group by":
+        row_max = np.full(n, -np.inf)
+        np.maximum.at(row_max, ii, s)                              # SELECT i, MAX(s) GROUP BY i
+        m = row_max[ii]                                            # JOIN row_max ON s.i = r.i
+    elif spelling == "window":
+        order = np.lexsort((jj, ii))
+        bounds = np.searchsorted(ii[order], np.arange(n + 1))
+        m = np.empty_like(s)
+        for i in range(n):                                         # one partition per i
+            idx = order[bounds[i]:bounds[i + 1]]
+            m[idx] = s[idx].max()
+    else:
+        raise ValueError(spelling)
+    w = np.exp(s - m)
+    z = np.zeros(n)
+    np.add.at(z, ii, w)                                            # norm: SUM(w) GROUP BY i
+    o = np.zeros((n, d))
+    np.add.at(o, ii, (w / z[ii])[:, None] * v[jj])                 # SUM(w / z * v) GROUP BY i, d
+    row_max = np.full(n, -np.inf)
+    np.maximum.at(row_max, ii, s)
+    return o, row_max + np.log(z)
+
+
+def loss(o: np.ndarray) -> float:
+    """SUM(x * x) / 2 over every output value."""
+    o = np.asarray(o, dtype=np.float64)
+    return float(np.sum(o * o) / 2)
+
+
+def backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray | None = None,
+                  scale: float = DEFAULT_SCALE, block: int = 256, route_max: bool = False):
+    """Gradients (dq, dk, dv) of sum_{i,d} dout_id * o_id; with dout = o (the
+    default) that is the gradient of loss = sum(o^2) / 2.  Closed-form chain
+    rule over the naive plan, recomputing each block's full score rows."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    n = q.shape[0]
+    if dout is None:
+        dout = forward_head(q, k, v, scale, block)[0]
+    dout = np.asarray(dout, dtype=np.float64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0 in range(0, n, block):
+        r1 = min(n, r0 + block)
+        present = _present(r0, r1, r1)
+        s = (q[r0:r1] @ k[:r1].T) * scale
+        masked = np.where(present, s, -np.inf)
+        m = masked.max(axis=1)
+        with np.errstate(invalid="ignore", over="ignore"):
+            w = np.where(present, np.exp(s - m[:, None]), 0.0)
+        z = w.sum(axis=1)
+        p = w / z[:, None]
+        dp = np.where(present, dout[r0:r1] @ v[:r1].T, 0.0)      # dL/dP_ij = dO_i . v_j
+        delta = np.sum(p * dp, axis=1)
+        ds = p * (dp - delta[:, None])                           # dL/ds_ij through w_ij
+        if route_max:
+            # m_i is itself max_j s_ij: dL/dm_i = -sum_j dS_ij goes to the argmax pair.
+            arg = np.argmax(masked, axis=1)
+            ds[np.arange(r1 - r0), arg] += -ds.sum(axis=1)
+        dq[r0:r1] = (ds @ k[:r1]) * scale
+        dk[:r1] += (ds.T @ q[r0:r1]) * scale
+        dv[:r1] += p.T @ dout[r0:r1]
+    return dq, dk, dv
+
+
+def _map_heads(fn, arrays, workers):
+    b, h = arrays[0].shape[:2]
+    jobs = [(bi, hi) for bi in range(b) for hi in range(h)]
+    if workers is None or workers <= 1:
+        return jobs, [fn(*(a[bi, hi] for a in arrays)) for bi, hi in jobs]
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        return jobs, list(ex.map(lambda j: fn(*(a[j[0], j[1]] for a in arrays)), jobs))
+
+
+def forward(q, k, v, scale: float = DEFAULT_SCALE, workers: int | None = None, block: int = 256):
+    """[B, H, N, D] float64 -> (o [B, H, N, D], lse [B, H, N]); heads are independent."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    o = np.empty_like(q)
+    lse = np.empty(q.shape[:3])
+    jobs, res = _map_heads(lambda a, b_, c: forward_head(a, b_, c, scale, block), (q, k, v), workers)
+    for (bi, hi), (oh, lh, _, _) in zip(jobs, res):
+        o[bi, hi] = oh
+        lse[bi, hi] = lh
+    return o, lse
+
+
+def backward(q, k, v, dout=None, scale: float = DEFAULT_SCALE, workers: int | None = None,
+             block: int = 256):
+    """[B, H, N, D] float64 -> (dq, dk, dv); dout defaults to the oracle's own o."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    if dout is None:
+        arrays = (q, k, v)
+        fn = lambda a, b_, c: backward_head(a, b_, c, None, scale, block)
+    else:
+        arrays = (q, k, v, np.asarray(dout, dtype=np.float64))
+        fn = lambda a, b_, c, d_: backward_head(a, b_, c, d_, scale, block)
+    out = [np.empty_like(q) for _ in range(3)]
+    jobs, res = _map_heads(fn, arrays, workers)
+    for (bi, hi), grads in zip(jobs, res):
+        for dst, g in zip(out, grads):
+            dst[bi, hi] = g
+    return tuple(out)

@@ -1,0 +1,289 @@
+"""Pins for the oracle: checks against what the pages and the mathematics fix.
+
+Each ``check_*`` takes the oracle as a module-like object ``orc`` (with
+``forward_head``, ``forward_head_relational``, ``backward_head`` and
+``nw_average``) and raises ``AssertionError`` on failure.  ``test_oracle.py``
+runs them on the real oracle; ``test_oracle_mutants.py`` runs them on copies of
+the oracle with a mistake planted, and requires each mistake to fail one.
+
+Sources (pages): "Show HN: automatic deduction of FlashAttention kernel from 25
+lines of SQL" (neshdevtech.com) for the method, the mask rule, the loss and
+the control; the Wiki notes page (brainpick-2k7.pages.dev), softmax section,
+for the worked example.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+import brute
+from metrics import rel_err
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+S = 0.125
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- forward --
+
+def check_brute_force(orc):
+    """Brute force at 50 digits (no max shift) on tiny heads, D = 64 and D = 4."""
+    for n, d, seed in ((12, 64, 10), (16, 4, 11), (1, 64, 12)):
+        rng = _rng(seed)
+        q, k, v = (rng.normal(size=(n, d)) for _ in range(3))
+        o, lse = orc.forward_head(q, k, v, S, block=5)[:2]
+        bo, bl = brute.attention(q, k, v, S)
+        assert rel_err(o, brute.to_np(bo)) < 2e-14, ("o", n, d)
+        assert rel_err(lse, brute.to_np(bl)) < 2e-14, ("lse", n, d)
+
+
+def check_worked_example(orc):
+    """The worked example on the Wiki notes page: logits [3, 1, -2] give
+    exp(val - max) = 1.0, 0.1353..., 0.0067... (digits printed truncated).
+
+    Built as a 3-token head whose last row has exactly those scores: q_2 = 8 e_0
+    and k_j = logit_j e_0 with scale 1/8; one-hot values v_j = e_j make o_2 the
+    softmax row, and o_2 * z_2 the numerators."""
+    g = json.load(open(os.path.join(GOLDEN, "softmax_worked_example.json")))
+    logits = g["logits"]
+    n, d = 3, 64
+    q = np.zeros((n, d)); k = np.zeros((n, d)); v = np.zeros((n, d))
+    q[2, 0] = 8.0
+    for j, x in enumerate(logits):
+        k[j, 0] = x
+        v[j, j] = 1.0
+    o, lse, m, z = orc.forward_head(q, k, v, S)
+    assert m[2] == g["max"]
+    numer = o[2, :3] * z[2]
+    for got, printed in zip(numer, g["exp_shifted_printed"]):
+        digits = len(printed.split(".")[1])
+        assert np.floor(got * 10 ** digits) / 10 ** digits == float(printed), (got, printed)
+    assert np.all(o[2, :3] > 0) and abs(o[2, :3].sum() - 1.0) < 1e-15
+    assert abs(lse[2] - np.log(np.sum(np.exp(np.array(logits))))) < 1e-15
+
+
+def check_token0(orc):
+    """Row 0 has one pair (0, 0): w = 1, z = 1, so o_0 = v_0 and lse_0 = s_00."""
+    rng = _rng(20)
+    q, k, v = (rng.normal(size=(33, 64)) for _ in range(3))
+    o, lse = orc.forward_head(q, k, v, S, block=8)[:2]
+    assert np.array_equal(o[0], v[0])
+    assert abs(lse[0] - (q[0] @ k[0]) * S) < 1e-15 * max(1.0, abs(lse[0]))
+
+
+def check_equal_scores(orc):
+    """Q = 0: every score is 0, so o_i is the mean of v_0..v_i and lse_i = ln(i+1)."""
+    rng = _rng(21)
+    n = 70
+    k, v = rng.normal(size=(n, 64)), rng.normal(size=(n, 64))
+    o, lse = orc.forward_head(np.zeros((n, 64)), k, v, S, block=16)[:2]
+    means = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    assert rel_err(o, means) < 1e-14
+    assert rel_err(lse, np.log(np.arange(1, n + 1))) < 1e-15
+
+
+def check_rows_sum_to_one(orc):
+    """Weights of a row sum to 1: constant v rows give that constant."""
+    rng = _rng(22)
+    n = 50
+    q, k = rng.normal(size=(n, 64)) * 3, rng.normal(size=(n, 64)) * 3
+    c = rng.normal(size=64)
+    o = orc.forward_head(q, k, np.tile(c, (n, 1)), S, block=12)[0]
+    assert rel_err(o, np.tile(c, (n, 1))) < 1e-14
+
+
+def check_prefix(orc):
+    """Output row i depends only on tokens <= i."""
+    rng = _rng(23)
+    n, t = 60, 23
+    q, k, v = (rng.normal(size=(n, 64)) for _ in range(3))
+    o_full = orc.forward_head(q, k, v, S, block=16)[0]
+    o_pre = orc.forward_head(q[:t], k[:t], v[:t], S, block=16)[0]
+    assert rel_err(o_full[:t], o_pre) < 1e-15
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    q2[t:] = rng.normal(size=(n - t, 64)); k2[t:] *= -3; v2[t:] += 5
+    o2 = orc.forward_head(q2, k2, v2, S, block=16)[0]
+    assert rel_err(o2[:t], o_full[:t]) < 1e-15
+    assert rel_err(o2[t:], o_full[t:]) > 1e-3
+
+
+def check_linearity(orc):
+    rng = _rng(24)
+    q, k, v = (rng.normal(size=(40, 64)) for _ in range(3))
+    o = orc.forward_head(q, k, v, S)[0]
+    assert rel_err(orc.forward_head(q, k, -2.5 * v, S)[0], -2.5 * o) < 1e-14
+
+
+def check_k_shift(orc):
+    """Adding c to every key adds q_i . c * scale to every score of row i: it
+    cancels from the softmax (o unchanged) and shifts lse_i by that amount."""
+    rng = _rng(25)
+    n = 45
+    q, k, v = (rng.normal(size=(n, 64)) for _ in range(3))
+    c = rng.normal(size=64)
+    o, lse = orc.forward_head(q, k, v, S)[:2]
+    o2, lse2 = orc.forward_head(q, k + c, v, S)[:2]
+    assert rel_err(o2, o) < 1e-13
+    assert rel_err(lse2, lse + (q @ c) * S) < 1e-13
+
+
+def _check_inf_pattern(o, j, col):
+    assert np.isfinite(o[:j]).all()
+    assert np.isposinf(o[j:, col]).all()
+    others = np.delete(o, col, axis=1)
+    assert np.isfinite(others).all()
+
+
+def check_inf_rule(orc):
+    """An infinity in V at token j reaches only rows i >= j (masks are absent
+    rows).  The page's case (n = 16, j = 9, feature 0, seed 1) and the
+    256-token fp64 workload with V[100, 5] = +inf."""
+    import causal_softmax_attention_amd.inputs as inp
+    q, k, v, j = inp.page_mask_inputs()
+    o, lse = orc.forward_head(q, k, v, S, block=4)[:2]
+    _check_inf_pattern(o, j, 0)
+    assert np.isfinite(lse).all()
+    a = inp.workload("fp64_256")
+    q, k, v = (a.as_f64(x)[0, 0] for x in "qkv")
+    v[100, 5] = np.inf
+    o, lse = orc.forward_head(q, k, v, S, block=64)[:2]
+    _check_inf_pattern(o, 100, 5)
+    assert np.isfinite(lse).all()
+
+
+def check_spellings_agree(orc):
+    """Window and GROUP BY spellings, matrix and relational forms, on the
+    demo's own inputs (n = 64 and 256, seed 0)."""
+    import causal_softmax_attention_amd.inputs as inp
+    for n, (q, k, v) in inp.page_sizes_inputs().items():
+        o, lse = orc.forward_head(q, k, v, S, block=100)[:2]
+        for spelling in ("window", "group by"):
+            o2, l2 = orc.forward_head_relational(q, k, v, S, spelling)
+            assert rel_err(o2, o) < 1e-14, (n, spelling)
+            assert rel_err(l2, lse) < 1e-14, (n, spelling)
+
+
+# --------------------------------------------------------------- backward --
+
+def check_grad_brute_fd(orc):
+    """Gradients of sum(o^2)/2 against 50-digit central differences of the
+    brute-force forward."""
+    for n, d, seed in ((6, 4, 30), (4, 8, 31)):
+        rng = _rng(seed)
+        q, k, v = (rng.normal(size=(n, d)) * 1.5 for _ in range(3))
+        got = orc.backward_head(q, k, v, None, S, block=3)
+        want = brute.grad_fd(q, k, v, S)
+        for name, g, w in zip("qkv", got, want):
+            assert rel_err(g, w) < 1e-13, ("d" + name, n, d, rel_err(g, w))
+
+
+def check_grad_fd64(orc):
+    """At the real D = 64: central differences (float64) of the loss evaluated
+    through the forward, on a sample of entries."""
+    rng = _rng(32)
+    n = 16
+    q, k, v = (rng.normal(size=(n, 64)) for _ in range(3))
+    dq, dk, dv = orc.backward_head(q, k, v, None, S, block=5)
+
+    def L(q_, k_, v_):
+        o = orc.forward_head(q_, k_, v_, S)[0]
+        return np.sum(o * o) / 2
+
+    h = 1e-6
+    for which, g in zip(range(3), (dq, dk, dv)):
+        for (r, c) in [(0, 0), (3, 17), (9, 63), (15, 5), (15, 40), (7, 7)]:
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][r, c] += h
+            lp = L(*args)
+            args[which][r, c] -= 2 * h
+            lm = L(*args)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[r, c]) < 2e-7 * max(1.0, np.abs(g).max()), (which, r, c, fd, g[r, c])
+
+
+def check_grad_invariants(orc):
+    """The max shift's gradient sums to zero, so each row of dS sums to 0 and
+    sum_j dK_j = 0; rows of P sum to 1, so sum_j dV_j = sum_i dO_i; row 0 has
+    a single pair, so dQ_0 = 0; routing the max's own gradient to the argmax
+    changes nothing."""
+    rng = _rng(33)
+    n = 48
+    q, k, v = (rng.normal(size=(n, 64)) * 2 for _ in range(3))
+    o = orc.forward_head(q, k, v, S)[0]
+    dq, dk, dv = orc.backward_head(q, k, v, None, S, block=10)
+    assert np.abs(dk.sum(axis=0)).max() < 1e-13 * n * np.abs(dk).max()
+    assert rel_err(dv.sum(axis=0), o.sum(axis=0)) < 1e-13
+    assert np.abs(dq[0]).max() < 1e-15 * np.abs(dq).max()
+    routed = orc.backward_head(q, k, v, None, S, block=10, route_max=True)
+    for a, b in zip(routed, (dq, dk, dv)):
+        assert rel_err(a, b) < 1e-13
+
+
+def check_grad_n1(orc):
+    rng = _rng(34)
+    q, k, v = (rng.normal(size=(1, 64)) for _ in range(3))
+    dq, dk, dv = orc.backward_head(q, k, v, None, S)
+    assert np.array_equal(dq, np.zeros_like(dq)) and np.array_equal(dk, np.zeros_like(dk))
+    assert rel_err(dv, v) < 1e-15
+
+
+def check_grad_q0(orc):
+    """Q = 0: P_ij = 1/(i+1); dK = 0 exactly; dV_j = sum_{i>=j} dO_i / (i+1)."""
+    rng = _rng(35)
+    n = 30
+    k, v, dout = (rng.normal(size=(n, 64)) for _ in range(3))
+    dq, dk, dv = orc.backward_head(np.zeros((n, 64)), k, v, dout, S, block=7)
+    assert np.array_equal(dk, np.zeros_like(dk))
+    scaled = dout / np.arange(1, n + 1)[:, None]
+    want = np.cumsum(scaled[::-1], axis=0)[::-1]
+    assert rel_err(dv, want) < 1e-14
+
+
+# --------------------------------------------------------------------- NW --
+
+def check_nw_brute(orc):
+    rng = _rng(40)
+    for nt, ns, span in ((5, 9, 1.0), (4, 7, 3.0)):
+        tx, ty = rng.uniform(0, span, nt), rng.uniform(0, span, nt)
+        sx, sy, sv = rng.uniform(0, span, ns), rng.uniform(0, span, ns), rng.normal(size=ns)
+        got = orc.nw_average(tx, ty, sx, sy, sv, 0.25)
+        assert rel_err(got, brute.nw(tx, ty, sx, sy, sv, 0.25)) < 1e-14
+
+
+def check_nw_special(orc):
+    """Constant values give the constant; one source gives its value; the
+    estimate is affine in the values."""
+    rng = _rng(41)
+    tx, ty = rng.uniform(0, 4, 20), rng.uniform(0, 4, 20)
+    sx, sy, sv = rng.uniform(0, 4, 50), rng.uniform(0, 4, 50), rng.normal(size=50)
+    assert rel_err(orc.nw_average(tx, ty, sx, sy, np.full(50, 2.5)), np.full(20, 2.5)) < 1e-15
+    assert rel_err(orc.nw_average(tx, ty, sx[:1], sy[:1], sv[:1]), np.full(20, sv[0])) < 1e-15
+    base = orc.nw_average(tx, ty, sx, sy, sv)
+    assert rel_err(orc.nw_average(tx, ty, sx, sy, 3 * sv - 1), 3 * base - 1) < 1e-14
+
+
+def check_nw_shift(orc):
+    """Subtracting the max cancels in exact arithmetic: on the demo's control
+    case (64 targets, 256 sources on [0, 1)^2, seed 2) the shifted and
+    unshifted forms agree; far from every source only the shifted one is finite."""
+    import causal_softmax_attention_amd.inputs as inp
+    a = inp.page_nw_inputs()
+    s = orc.nw_average(a.tx, a.ty, a.sx, a.sy, a.sv, 0.25, shift=True)
+    u = orc.nw_average(a.tx, a.ty, a.sx, a.sy, a.sv, 0.25, shift=False)
+    assert rel_err(s, u) < 1e-14
+    far = orc.nw_average(np.array([500.0]), np.array([500.0]), a.sx, a.sy, a.sv, 0.25)
+    assert np.isfinite(far).all() and a.sv.min() <= far[0] <= a.sv.max()
+
+
+ATTENTION_FORWARD_CHECKS = [check_brute_force, check_worked_example, check_token0,
+                            check_equal_scores, check_rows_sum_to_one, check_prefix,
+                            check_linearity, check_k_shift, check_inf_rule, check_spellings_agree]
+ATTENTION_BACKWARD_CHECKS = [check_grad_brute_fd, check_grad_fd64, check_grad_invariants,
+                             check_grad_n1, check_grad_q0]
+NW_CHECKS = [check_nw_brute, check_nw_special, check_nw_shift]
+ALL_CHECKS = ATTENTION_FORWARD_CHECKS + ATTENTION_BACKWARD_CHECKS + NW_CHECKS

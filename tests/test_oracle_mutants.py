@@ -1,0 +1,79 @@
+"""Each plausible mistake planted in a copy of the oracle must fail a pin.
+
+The oracle's source is read, one edit is applied, and the edited copy is run in
+a fresh module namespace (the real oracle is untouched).  A mutant passes the
+test only if at least one of the pins in oracle_pins.py rejects it.
+"""
+import os
+import types
+
+import pytest
+
+import oracle_pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _load(fname, edit):
+    src = open(os.path.join(ROOT, "oracle", fname)).read()
+    old, new, nth = edit
+    pos = -1
+    for _ in range(nth + 1):
+        pos = src.index(old, pos + 1)
+    src = src[:pos] + new + src[pos + len(old):]
+    mod = types.ModuleType("oracle_mutant_" + fname[:-3])
+    exec(compile(src, fname, "exec"), mod.__dict__)
+    return mod
+
+
+# (file, (old text, new text, which occurrence), checks that should catch it)
+MUTANTS = {
+    "diagonal dropped": ("attention.py", ("return j <= i", "return j < i", 0), "fwd"),
+    "one token of lookahead": ("attention.py", ("return j <= i", "return j <= i + 1", 0), "fwd"),
+    "scores transposed": ("attention.py", ("(q[r0:r1] @ k[:r1].T)", "(k[r0:r1] @ q[:r1].T)", 0), "fwd"),
+    "scale 1/4": ("attention.py", ("@ k[:r1].T) * scale", "@ k[:r1].T) * 0.25", 0), "fwd"),
+    "lse in log2": ("attention.py", ("lse[r0:r1] = m + np.log(z)", "lse[r0:r1] = m + np.log2(z)", 0), "fwd"),
+    "not normalised": ("attention.py", ("_sum_present(w / z[:, None],", "_sum_present(w,", 0), "fwd"),
+    "max added": ("attention.py", ("np.exp(s - m[:, None])", "np.exp(s + m[:, None])", 0), "fwd"),
+    "absent pairs multiplied": ("attention.py",
+                                ("out[:, d] += np.where(present[:, j], term, 0.0)",
+                                 "out[:, d] += np.nan_to_num(term, nan=0.0)", 0), "fwd"),
+    "group-by joined on j": ("attention.py", ("m = row_max[ii]", "m = row_max[jj]", 0), "fwd"),
+    "dS sign": ("attention.py", ("ds = p * (dp - delta[:, None])", "ds = p * (dp + delta[:, None])", 0), "bwd"),
+    "delta without P": ("attention.py", ("delta = np.sum(p * dp, axis=1)", "delta = np.sum(dp, axis=1)", 0), "bwd"),
+    "dQ unscaled": ("attention.py", ("dq[r0:r1] = (ds @ k[:r1]) * scale", "dq[r0:r1] = (ds @ k[:r1])", 0), "bwd"),
+    "dK from k": ("attention.py", ("(ds.T @ q[r0:r1])", "(ds.T @ k[r0:r1])", 0), "bwd"),
+    "dV from v": ("attention.py", ("dv[:r1] += p.T @ dout[r0:r1]", "dv[:r1] += p.T @ v[r0:r1]", 0), "bwd"),
+    "dP from k": ("attention.py", ("dout[r0:r1] @ v[:r1].T", "dout[r0:r1] @ k[:r1].T", 0), "bwd"),
+    "dS transposed in dQ": ("attention.py", ("(ds @ k[:r1])", "(ds.T[:r1 - r0, :] @ k[:r1])", 0), "bwd"),
+    "backward unmasked": ("attention.py", ("present = _present(r0, r1, r1)",
+                                           "present = np.ones((r1 - r0, r1), dtype=bool)", 1), "bwd"),
+    "bandwidth 2h^2": ("nw.py", ("/ denom", "/ (2 * denom)", 0), "nw"),
+    "y against x": ("nw.py", ("(ty[r0:r1, None] - sy[None, :])", "(ty[r0:r1, None] - sx[None, :])", 0), "nw"),
+    "mean of weights": ("nw.py", ("(w @ sv) / w.sum(axis=1)", "(w @ sv) / w.shape[1]", 0), "nw"),
+    "min subtracted": ("nw.py", ("e.max(axis=1, keepdims=True)", "e.min(axis=1, keepdims=True)", 0), "nw"),
+}
+
+GROUPS = {"fwd": oracle_pins.ATTENTION_FORWARD_CHECKS,
+          "bwd": oracle_pins.ATTENTION_BACKWARD_CHECKS,
+          "nw": oracle_pins.NW_CHECKS}
+
+
+@pytest.mark.parametrize("name", list(MUTANTS))
+def test_mutant_is_caught(name):
+    fname, edit, group = MUTANTS[name]
+    mod = _load(fname, edit)
+    import oracle
+    orc = types.SimpleNamespace(
+        forward_head=oracle.forward_head, forward_head_relational=oracle.forward_head_relational,
+        backward_head=oracle.backward_head, nw_average=oracle.nw_average)
+    for attr in ("forward_head", "forward_head_relational", "backward_head", "nw_average"):
+        if hasattr(mod, attr):
+            setattr(orc, attr, getattr(mod, attr))
+    caught = []
+    for check in GROUPS[group]:
+        try:
+            check(orc)
+        except Exception as e:  # noqa: BLE001 - any rejection counts
+            caught.append((check.__name__, type(e).__name__))
+    assert caught, f"mutant {name!r} passed every {group} pin"
