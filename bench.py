@@ -1,0 +1,283 @@
+"""Throughput of causal softmax attention fwd + bwd on one MI355X.
+
+One step = one forward and one backward pass (upstream gradient dO = O, the
+loss sum(o^2)/2) over the bfloat16 workload of 8 x 32 heads x 4096 tokens,
+D = 64, inputs resident in HBM before the timed region.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+                    [--no-secondary]
+
+value: algorithmic TFLOP/s of the whole step.  Algorithmic work counts only the
+N(N+1)/2 pairs (i, j <= i) of each head: 4 D flops per pair in the forward
+(Q K^T and P V) and 10 D in the backward (Q K^T recomputed, dO V^T, P^T dO,
+dS^T Q, dS K), 14 D = 896 flops per pair in all.
+
+roofline: the kernel with the largest share of the step, timed live with HIP
+events on the library's stream (the timer hook of the C ABI), against the
+bf16 dense MFMA peak of MI355X (2516.6 TFLOP/s).  traffic: HBM bytes per
+launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded in
+profiles/traffic.json, reported only while the kernel's source is unchanged
+since they were taken.
+
+cpu_baseline: the float64 oracle (test infrastructure, never tuned) on a
+bounded sample of whole heads of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK = 2516.6       # TFLOP/s, MI355X dense bf16 MFMA
+F32_PEAK = 157.3         # TFLOP/s, MI355X fp32 MFMA
+HBM_PEAK = 8000.0        # GB/s
+D = 64
+METRIC = "causal attn fwd+bwd TFLOP/s at N=4096 D=64 bf16; % of MFMA peak"
+
+# kernel slot -> (name in rocprofv3 output, source file, algorithmic flops per pair)
+KERNELS = {
+    "fwd": ("attn_fwd", 4 * D),
+    "bwd_dkdv": ("attn_bwd_dkdv", 8 * D),
+    "bwd_dq": ("attn_bwd_dq", 6 * D),
+}
+
+
+def pairs(heads: int, n: int) -> int:
+    return heads * n * (n + 1) // 2
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "causal_softmax_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(slot: str, launches_per_kernel=1):
+    """HBM bytes per launch of `slot` from profiles/traffic.json, if current."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(slot)
+    if not rec:
+        return None
+    if rec.get("source_sha") != source_sha(rec["sources"]):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def make_inputs(name):
+    import numpy as np
+    import torch
+
+    import causal_softmax_attention_amd.inputs as inp
+    a = inp.workload(name)
+    dt = {"bf16": torch.bfloat16, "f32": torch.float32, "f64": torch.float64}[a.dtype]
+
+    def dev(x):
+        if a.dtype == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        return torch.from_numpy(x).to("cuda:0")
+    return a, [dev(getattr(a, x)) for x in "qkv"], dt
+
+
+def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True):
+    """Run `steps` timed steps; returns (ms_per_step, {slot: mean ms}, outputs)."""
+    import torch
+
+    import causal_softmax_attention_amd as csa
+    B, H, N, _ = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32 if q.dtype != torch.float64 else torch.float64,
+                      device=q.device)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    code = {torch.bfloat16: csa.ATTN_BF16, torch.float32: csa.ATTN_F32,
+            torch.float64: csa.ATTN_F64}[q.dtype]
+    ws = torch.empty(max(16, csa.attn_causal_bwd_workspace_bytes(code, B, H, N, D)),
+                     dtype=torch.uint8, device=q.device)
+
+    def step():
+        csa.attn_causal_fwd(q, k, v, 0.125, o=o, lse=lse)
+        if with_bwd:
+            csa.attn_causal_bwd(q, k, v, o, o, lse, 0.125, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    slots = [csa.TIMER_FWD] + ([csa.TIMER_BWD_PRE, csa.TIMER_BWD_DKDV, csa.TIMER_BWD_DQ]
+                               if with_bwd else [])
+    events = []
+    if per_kernel:
+        for _ in range(steps):
+            ev = {}
+            for s in slots:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(); b.record()            # materialise the HIP events
+                ev[s] = (a, b)
+            events.append(ev)
+        torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        if per_kernel:
+            for s in slots:
+                csa.attn_set_kernel_timer(s, *events[i][s])
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    for s in slots:
+        csa.attn_set_kernel_timer(s, None, None)
+    ms = start.elapsed_time(stop) / steps
+    per = {}
+    if per_kernel:
+        for s in slots:
+            per[csa.TIMER_NAMES[s]] = sum(e[s][0].elapsed_time(e[s][1]) for e in events) / steps
+    return ms, wall, per, (o, lse)
+
+
+def cpu_baseline(a, budget_s=10.0):
+    """The oracle on whole heads of the workload until ~budget_s of CPU work."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i["num_threads"] for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    B, H, N = a.q.shape[:3]
+    done, t0 = 0, time.perf_counter()
+    order = [(b, h) for b in range(B) for h in range(H)]
+    while done < len(order):
+        b, h = order[done]
+        q, k, v = (a.as_f64(x)[b, h] for x in "qkv")
+        oracle.forward_head(q, k, v, 0.125)
+        oracle.backward_head(q, k, v, None, 0.125)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    flops = 14 * D * pairs(done, N)
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {B * H} heads (N={N}), float64 fwd + bwd, {el:.1f} s wall; "
+                      f"BLAS threads={threads}, elementwise numpy single-threaded"}
+
+
+def secondary(steps):
+    """Other workloads: fp32 forward, long-sequence bf16 fwd+bwd, NW control, fp64 latency."""
+    import numpy as np
+    import torch
+
+    import causal_softmax_attention_amd as csa
+    import causal_softmax_attention_amd.inputs as inp
+    out = {}
+    a, (q, k, v), _ = make_inputs("fp32_2k")
+    ms, _, per, _ = time_attention(q, k, v, steps, 2, with_bwd=False)
+    fl = 4 * D * pairs(64, 2048)
+    out["fp32_2k_fwd"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
+                          "frac_of_fp32_mfma_peak": fl / ms / 1e9 / F32_PEAK}
+    del q, k, v
+    a, (q, k, v), _ = make_inputs("bf16_32k")
+    ms, _, per, _ = time_attention(q, k, v, max(2, steps // 4), 1)
+    fl = 14 * D * pairs(16, 32768)
+    out["bf16_32k_fwd_bwd"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
+                               "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
+                               "kernels_ms": per}
+    del q, k, v
+    a, (q, k, v), _ = make_inputs("fp64_256")
+    ms, _, per, _ = time_attention(q, k, v, steps, 2)
+    out["fp64_256_fwd_bwd"] = {"us": ms * 1e3, "kernels_us": {k_: v_ * 1e3 for k_, v_ in per.items()}}
+    nw = inp.nw_inputs()
+    cols = [torch.from_numpy(x).to("cuda:0") for x in (nw.tx, nw.ty, nw.sx, nw.sy, nw.sv)]
+    res = torch.empty_like(cols[0])
+    for _ in range(2):
+        csa.nw_gauss_average(*cols, 0.25, out=res)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        csa.nw_gauss_average(*cols, 0.25, out=res)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    out["nw_64k"] = {"ms": ms, "Gpairs/s": 65536.0 ** 2 / ms / 1e6}
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this library has no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_softmax_attention_amd as csa
+    if not os.path.exists(csa.LIB_PATH):
+        from causal_softmax_attention_amd import _build
+        _build.build()
+    csa.lib()
+    log("generating bf16_4k inputs")
+    a, (q, k, v), _ = make_inputs("bf16_4k")
+    B, H, N = q.shape[:3]
+    log(f"timing {args.steps} steps after {args.warmup} warmup")
+    ms, wall, per, _ = time_attention(q, k, v, args.steps, args.warmup)
+    flops = 14 * D * pairs(B * H, N)
+    value = flops / ms / 1e9
+    # dominant kernel
+    algo = {"fwd": 4 * D, "bwd_dkdv": 8 * D, "bwd_dq": 6 * D, "bwd_pre": 0}
+    dom = max((s for s in per if algo.get(s)), key=lambda s: per[s])
+    kflops = algo[dom] * pairs(B * H, N)
+    achieved = kflops / per[dom] / 1e9
+    roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK,
+            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK, 4),
+            "traffic": traffic_for(dom), "kernel_ms": round(per[dom], 4),
+            "algorithmic_flops_per_launch": kflops}
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v; no dataset)",
+        "config": {"workload": "bf16_4k: causal attention fwd+bwd, B=8 H=32 N=4096 D=64, "
+                               "scale 1/8, dO = O", "global_batch": B, "heads": H, "seq_len": N,
+                   "head_dim": D, "parallelism": "none (1 GPU)"},
+        "frac_of_bf16_mfma_peak": round(value / BF16_PEAK, 4),
+        "wall_ms_per_step": round(wall, 4),
+        "kernels_ms": {k_: round(v_, 4) for k_, v_ in per.items()},
+        "roofline": roof,
+    }
+    del q, k, v
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        log("secondary workloads")
+        rec["secondary"] = secondary(max(3, args.steps // 2))
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        rec["cpu_baseline"] = cpu_baseline(a, args.cpu_budget)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+"""Causal softmax attention (D = 64) and the Nadaraya-Watson control on MI355X.
+
+A thin ctypes binding over the C ABI in ``include/attn.h`` (``libattn.so``,
+built in-tree by ``python -m causal_softmax_attention_amd._build``).  The
+functions here carry the C entry points' names and only marshal arguments:
+torch supplies device memory and the current stream; every step of the
+computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or fails, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+ATTN_F64, ATTN_F32, ATTN_BF16 = 0, 1, 2
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+DEFAULT_SCALE = 0.125
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+_LIB = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m causal_softmax_attention_amd._build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        L.attn_causal_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
+                                      vp, vp, vp, vp, vp, vp]
+        L.attn_causal_fwd.restype = ctypes.c_int
+        L.attn_causal_bwd_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+        L.attn_causal_bwd_workspace_bytes.restype = sz
+        L.attn_causal_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
+                                      vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_causal_bwd.restype = ctypes.c_int
+        L.nw_gauss_average.argtypes = [i64, vp, vp, i64, vp, vp, vp, ctypes.c_float, vp, vp]
+        L.nw_gauss_average.restype = ctypes.c_int
+        L.attn_set_kernel_timer.argtypes = [ctypes.c_int, vp, vp]
+        L.attn_set_kernel_timer.restype = ctypes.c_int
+        L.attn_last_error.argtypes = []
+        L.attn_last_error.restype = ctypes.c_char_p
+        _LIB = L
+    return _LIB
+
+
+def attn_last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != ATTN_OK:
+        raise AttnError(rc, attn_last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float64: ATTN_F64, torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _stream(t, stream):
+    import torch
+    s = torch.cuda.current_stream(t.device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _bhnd(t, name):
+    if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous [B, H, N, D] device tensor")
+    return t.shape
+
+
+def attn_causal_fwd(q, k, v, scale: float = DEFAULT_SCALE, o=None, lse=None, stream=None):
+    """Forward pass; returns (o, lse).  q, k, v: [B, H, N, 64] float64/float32/bfloat16."""
+    import torch
+    B, H, N, D = _bhnd(q, "q")
+    for name, t in (("k", k), ("v", v)):
+        if _bhnd(t, name) != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float64 if q.dtype == torch.float64 else torch.float32,
+                          device=q.device)
+    _check(lib().attn_causal_fwd(_dtype_code(q), B, H, N, D, float(scale), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(o), _ptr(lse), _stream(q, stream)))
+    return o, lse
+
+
+def attn_causal_bwd_workspace_bytes(dtype_code: int, B: int, H: int, N: int, D: int = 64) -> int:
+    return int(lib().attn_causal_bwd_workspace_bytes(dtype_code, B, H, N, D))
+
+
+def attn_causal_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, dq=None, dk=None,
+                    dv=None, workspace=None, stream=None):
+    """Backward pass; returns (dq, dk, dv).  Pass dout = o for the loss sum(o^2)/2."""
+    import torch
+    B, H, N, D = _bhnd(q, "q")
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if _bhnd(t, name) != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    code = _dtype_code(q)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    need = attn_causal_bwd_workspace_bytes(code, B, H, N, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().attn_causal_bwd(code, B, H, N, D, float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(q, stream)))
+    return dq, dk, dv
+
+
+def nw_gauss_average(tx, ty, sx, sy, sv, denom: float = 0.25, out=None, stream=None):
+    """Nadaraya-Watson average at every target; float32 1-D device tensors."""
+    import torch
+    for name, t in (("tx", tx), ("ty", ty), ("sx", sx), ("sy", sy), ("sv", sv)):
+        if t.dim() != 1 or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous 1-D float32 device tensor")
+    if ty.shape != tx.shape or sy.shape != sx.shape or sv.shape != sx.shape:
+        raise ValueError("target columns and source columns must have matching lengths")
+    if out is None:
+        out = torch.empty_like(tx)
+    _check(lib().nw_gauss_average(tx.numel(), _ptr(tx), _ptr(ty), sx.numel(), _ptr(sx),
+                                  _ptr(sy), _ptr(sv), float(denom), _ptr(out),
+                                  _stream(tx, stream)))
+    return out
+
+
+TIMER_FWD, TIMER_BWD_PRE, TIMER_BWD_DKDV, TIMER_BWD_DQ, TIMER_NW = range(5)
+TIMER_NAMES = {TIMER_FWD: "fwd", TIMER_BWD_PRE: "bwd_pre", TIMER_BWD_DKDV: "bwd_dkdv",
+               TIMER_BWD_DQ: "bwd_dq", TIMER_NW: "nw"}
+
+
+def attn_set_kernel_timer(slot: int, start, stop):
+    """Record two already-recorded torch.cuda.Event objects (or None, None)
+    around every later launch of the kernel in ``slot`` (TIMER_*)."""
+    h = (lambda e: None if e is None else ctypes.c_void_p(e.cuda_event))
+    _check(lib().attn_set_kernel_timer(slot, h(start), h(stop)))
+
+
+__all__ = ["attn_causal_fwd", "attn_causal_bwd", "attn_causal_bwd_workspace_bytes",
+           "nw_gauss_average", "attn_set_kernel_timer", "attn_last_error", "lib", "AttnError",
+           "ATTN_F64", "ATTN_F32", "ATTN_BF16"]

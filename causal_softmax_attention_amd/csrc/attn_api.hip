@@ -1,0 +1,194 @@
+// C ABI of the library (declared in include/attn.h): argument checks, dtype
+// dispatch, and error reporting.  Every check happens before any launch.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/attn.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local attn::Timers g_tm;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) {
+    g_err.clear();
+    return ATTN_OK;
+  }
+  return fail(ATTN_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t elem_size(int dtype) { return dtype == ATTN_BF16 ? 2 : dtype == ATTN_F32 ? 4 : 8; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+// Largest sizes the kernels index: a head's element count and the total
+// element count must fit the int/int64 arithmetic used on the device.
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxHeads = int64_t(1) << 24;
+
+int check_sizes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale) {
+  if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_EINVAL, "unknown dtype %d", dtype);
+  if (B < 1 || H < 1 || N < 1 || D < 1)
+    return fail(ATTN_EINVAL, "sizes must be >= 1 (B=%lld H=%lld N=%lld D=%lld)", (long long)B,
+                (long long)H, (long long)N, (long long)D);
+  if (D != 64) return fail(ATTN_EUNSUPPORTED, "D=%lld: only D=64 is implemented", (long long)D);
+  if (N > kMaxN) return fail(ATTN_EINVAL, "N=%lld exceeds %lld", (long long)N, (long long)kMaxN);
+  if (B > kMaxHeads / H)
+    return fail(ATTN_EINVAL, "B*H exceeds %lld", (long long)kMaxHeads);
+  if (!(scale > 0.0) || !isfinite(scale)) return fail(ATTN_EINVAL, "scale must be finite and > 0");
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                    const void* q, const void* k, const void* v, void* o, void* lse,
+                    void* stream) {
+  if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
+  if (!q || !k || !v || !o || !lse) return fail(ATTN_EINVAL, "null pointer argument");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return fail(ATTN_EINVAL, "pointers must be 16-byte aligned");
+  const int64_t heads = B * H;
+  const size_t tb = (size_t)heads * N * D * elem_size(dtype);
+  const size_t lb = (size_t)heads * N * (dtype == ATTN_F64 ? 8 : 4);
+  const void* ins[3] = {q, k, v};
+  for (const void* p : ins)
+    if (overlap(o, tb, p, tb) || overlap(lse, lb, p, tb))
+      return fail(ATTN_EINVAL, "outputs must not alias inputs");
+  if (overlap(o, tb, lse, lb)) return fail(ATTN_EINVAL, "o and lse overlap");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (dtype) {
+    case ATTN_F64:
+      e = attn::launch_fwd<double>((const double*)q, (const double*)k, (const double*)v,
+                                   (double*)o, lse, heads, N, scale, s, g_tm);
+      break;
+    case ATTN_F32:
+      e = attn::launch_fwd<float>((const float*)q, (const float*)k, (const float*)v, (float*)o,
+                                  lse, heads, N, scale, s, g_tm);
+      break;
+    default:
+      e = attn::launch_fwd<__bf16>((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                                   (__bf16*)o, lse, heads, N, scale, s, g_tm);
+  }
+  return hip_status(e, "attn_causal_fwd launch");
+}
+
+size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
+  if (check_sizes(dtype, B, H, N, D, 1.0) != ATTN_OK) return 0;
+  const int64_t heads = B * H;
+  switch (dtype) {
+    case ATTN_F64: return attn::bwd_workspace_bytes<double>(heads, N);
+    case ATTN_F32: return attn::bwd_workspace_bytes<float>(heads, N);
+    default: return attn::bwd_workspace_bytes<__bf16>(heads, N);
+  }
+}
+
+int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                    const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const void* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return fail(ATTN_EINVAL, "null pointer argument");
+  const void* all[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : all)
+    if (!aligned16(p)) return fail(ATTN_EINVAL, "pointers must be 16-byte aligned");
+  const size_t need = attn_causal_bwd_workspace_bytes(dtype, B, H, N, D);
+  if (workspace_bytes < need)
+    return fail(ATTN_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
+                workspace_bytes, need);
+  const int64_t heads = B * H;
+  const size_t tb = (size_t)heads * N * D * elem_size(dtype);
+  const size_t lb = (size_t)heads * N * (dtype == ATTN_F64 ? 8 : 4);
+  const void* ins[] = {q, k, v, o, dout};
+  void* outs[] = {dq, dk, dv};
+  for (void* w : outs) {
+    for (const void* r : ins)
+      if (overlap(w, tb, r, tb)) return fail(ATTN_EINVAL, "outputs must not alias inputs");
+    if (overlap(w, tb, lse, lb) || overlap(w, tb, workspace, need))
+      return fail(ATTN_EINVAL, "outputs must not alias lse or the workspace");
+  }
+  if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb))
+    return fail(ATTN_EINVAL, "dq, dk and dv must not overlap");
+  for (const void* r : ins)
+    if (overlap(workspace, need, r, tb)) return fail(ATTN_EINVAL, "workspace aliases an input");
+  if (overlap(workspace, need, lse, lb)) return fail(ATTN_EINVAL, "workspace aliases lse");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (dtype) {
+    case ATTN_F64:
+      e = attn::launch_bwd<double>((const double*)q, (const double*)k, (const double*)v,
+                                   (const double*)o, (const double*)dout, lse, (double*)dq,
+                                   (double*)dk, (double*)dv, workspace, heads, N, scale, s, g_tm);
+      break;
+    case ATTN_F32:
+      e = attn::launch_bwd<float>((const float*)q, (const float*)k, (const float*)v,
+                                  (const float*)o, (const float*)dout, lse, (float*)dq,
+                                  (float*)dk, (float*)dv, workspace, heads, N, scale, s, g_tm);
+      break;
+    default:
+      e = attn::launch_bwd<__bf16>((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                                   (const __bf16*)o, (const __bf16*)dout, lse, (__bf16*)dq,
+                                   (__bf16*)dk, (__bf16*)dv, workspace, heads, N, scale, s, g_tm);
+  }
+  return hip_status(e, "attn_causal_bwd launch");
+}
+
+int nw_gauss_average(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,
+                     const float* sx, const float* sy, const float* sv, float denom,
+                     float* out, void* stream) {
+  if (n_targets < 1 || n_sources < 1)
+    return fail(ATTN_EINVAL, "n_targets and n_sources must be >= 1");
+  if (n_targets > (int64_t(1) << 30) || n_sources > (int64_t(1) << 30))
+    return fail(ATTN_EINVAL, "at most 2^30 targets and sources");
+  if (!(denom > 0.f) || !isfinite(denom)) return fail(ATTN_EINVAL, "denom must be finite and > 0");
+  if (!tx || !ty || !sx || !sy || !sv || !out) return fail(ATTN_EINVAL, "null pointer argument");
+  const void* cols[] = {tx, ty, sx, sy, sv, out};
+  for (const void* p : cols)
+    if ((uintptr_t)p & 3u) return fail(ATTN_EINVAL, "pointers must be 4-byte aligned");
+  const size_t tb = (size_t)n_targets * 4, sb = (size_t)n_sources * 4;
+  if (overlap(out, tb, tx, tb) || overlap(out, tb, ty, tb) || overlap(out, tb, sx, sb) ||
+      overlap(out, tb, sy, sb) || overlap(out, tb, sv, sb))
+    return fail(ATTN_EINVAL, "out must not alias an input");
+  hipError_t e = attn::launch_nw(n_targets, tx, ty, n_sources, sx, sy, sv, denom, out,
+                                 (hipStream_t)stream, g_tm);
+  return hip_status(e, "nw_gauss_average launch");
+}
+
+int attn_set_kernel_timer(int slot, void* start, void* stop) {
+  if (slot < 0 || slot >= ATTN_TIMER_SLOTS) return fail(ATTN_EINVAL, "unknown timer slot %d", slot);
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(ATTN_EINVAL, "pass both events or neither");
+  g_tm.start[slot] = (hipEvent_t)start;
+  g_tm.stop[slot] = (hipEvent_t)stop;
+  g_err.clear();
+  return ATTN_OK;
+}
+
+const char* attn_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

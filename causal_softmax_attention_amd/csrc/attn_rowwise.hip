@@ -1,0 +1,262 @@
+// Row-per-lane causal attention, forward and backward, for every storage type.
+//
+// One lane owns one query row (forward, dQ) or one key row (dK/dV) and walks
+// the other side's rows through LDS tiles, so every pair (i, j) with j <= i is
+// visited by exactly the lanes that own it and an absent pair (j > i) is never
+// touched (pages: "Show HN: automatic deduction of FlashAttention kernel from
+// 25 lines of SQL", the join predicate q.t >= k.t and the masks-are-absent-rows
+// check).  The forward keeps a running max and denominator per row (the
+// streaming plan the same page attributes to FlashAttention) and stores
+// lse = m + ln l for the backward.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kRows = 64;   // rows per workgroup (one wave)
+constexpr int kTile = 32;   // rows of the streamed side per LDS tile
+
+template <typename T>
+__global__ __launch_bounds__(kRows) void fwd_rowwise(const T* __restrict__ q,
+                                                      const T* __restrict__ k,
+                                                      const T* __restrict__ v, T* __restrict__ o,
+                                                      acc_t<T>* __restrict__ lse, int N,
+                                                      int nqb, acc_t<T> scale) {
+  using A = acc_t<T>;
+  __shared__ A ks[kTile][kD];
+  __shared__ A vs[kTile][kD];
+  const int head = blockIdx.x / nqb;
+  const int qb = nqb - 1 - (blockIdx.x % nqb);  // longest rows first
+  const size_t base = (size_t)head * N * kD;
+  const int i = qb * kRows + threadIdx.x;
+  const bool valid = i < N;
+
+  A qr[kD], acc[kD];
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    qr[d] = valid ? widen(q[base + (size_t)i * kD + d]) : A(0);
+    acc[d] = 0;
+  }
+  A m = neg_inf<A>(), l = 0;
+  const int kend = min(N, (qb + 1) * kRows);
+  for (int k0 = 0; k0 < kend; k0 += kTile) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kTile * kD; e += kRows) {
+      const int r = e / kD, c = e % kD, j = k0 + r;
+      ks[r][c] = j < N ? widen(k[base + (size_t)j * kD + c]) : A(0);
+      vs[r][c] = j < N ? widen(v[base + (size_t)j * kD + c]) : A(0);
+    }
+    __syncthreads();
+    const int jn = min(kTile, kend - k0);
+    for (int jj = 0; jj < jn; ++jj) {
+      if (k0 + jj > i) break;  // pairs j > i do not exist
+      A s = 0;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) s += qr[d] * ks[jj][d];
+      s *= scale;
+      if (s > m) {
+        const A alpha = exp_acc(m - s);
+        l *= alpha;
+#pragma unroll
+        for (int d = 0; d < kD; ++d) acc[d] *= alpha;
+        m = s;
+      }
+      const A p = exp_acc(s - m);
+      l += p;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) acc[d] += p * vs[jj][d];
+    }
+  }
+  if (valid) {
+    const A inv = A(1) / l;
+#pragma unroll
+    for (int d = 0; d < kD; ++d) o[base + (size_t)i * kD + d] = narrow<T>(acc[d] * inv);
+    lse[(size_t)head * N + i] = m + log_acc(l);
+  }
+}
+
+// delta_i = sum_d dout_id * o_id
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_delta(const T* __restrict__ o, const T* __restrict__ dout,
+                                                 acc_t<T>* __restrict__ delta, int64_t rows) {
+  using A = acc_t<T>;
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  A s = 0;
+#pragma unroll 8
+  for (int d = 0; d < kD; ++d) s += widen(o[r * kD + d]) * widen(dout[r * kD + d]);
+  delta[r] = s;
+}
+
+// dK, dV: one lane per key j, queries i >= j streamed through LDS.
+template <typename T>
+__global__ __launch_bounds__(kRows) void bwd_dkdv_rowwise(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
+    const acc_t<T>* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int N, int nkb,
+    acc_t<T> scale) {
+  using A = acc_t<T>;
+  __shared__ A qs[kTile][kD];
+  __shared__ A dos[kTile][kD];
+  __shared__ A ls[kTile], ds_[kTile];
+  const int head = blockIdx.x / nkb;
+  const int kb = blockIdx.x % nkb;  // low key blocks see the most queries: they come first
+  const size_t base = (size_t)head * N * kD;
+  const int j = kb * kRows + threadIdx.x;
+  const bool valid = j < N;
+  A kr[kD], vr[kD], gk[kD], gv[kD];
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    kr[d] = valid ? widen(k[base + (size_t)j * kD + d]) : A(0);
+    vr[d] = valid ? widen(v[base + (size_t)j * kD + d]) : A(0);
+    gk[d] = 0;
+    gv[d] = 0;
+  }
+  for (int q0 = kb * kRows; q0 < N; q0 += kTile) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kTile * kD; e += kRows) {
+      const int r = e / kD, c = e % kD, i = q0 + r;
+      qs[r][c] = i < N ? widen(q[base + (size_t)i * kD + c]) : A(0);
+      dos[r][c] = i < N ? widen(dout[base + (size_t)i * kD + c]) : A(0);
+    }
+    if (threadIdx.x < kTile) {
+      const int i = q0 + threadIdx.x;
+      ls[threadIdx.x] = i < N ? lse[(size_t)head * N + i] : A(0);
+      ds_[threadIdx.x] = i < N ? delta[(size_t)head * N + i] : A(0);
+    }
+    __syncthreads();
+    const int in = min(kTile, N - q0);
+    for (int ii = 0; ii < in; ++ii) {
+      if (q0 + ii < j) continue;  // pair (i, j) exists only for i >= j
+      A s = 0, dp = 0;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) {
+        s += qs[ii][d] * kr[d];
+        dp += dos[ii][d] * vr[d];
+      }
+      const A p = exp_acc(s * scale - ls[ii]);
+      const A dsc = p * (dp - ds_[ii]) * scale;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) {
+        gv[d] += p * dos[ii][d];
+        gk[d] += dsc * qs[ii][d];
+      }
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int d = 0; d < kD; ++d) {
+      dk[base + (size_t)j * kD + d] = narrow<T>(gk[d]);
+      dv[base + (size_t)j * kD + d] = narrow<T>(gv[d]);
+    }
+  }
+}
+
+// dQ: one lane per query i, keys j <= i streamed through LDS.
+template <typename T>
+__global__ __launch_bounds__(kRows) void bwd_dq_rowwise(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
+    const acc_t<T>* __restrict__ delta, T* __restrict__ dq, int N, int nqb, acc_t<T> scale) {
+  using A = acc_t<T>;
+  __shared__ A ks[kTile][kD];
+  __shared__ A vs[kTile][kD];
+  const int head = blockIdx.x / nqb;
+  const int qb = nqb - 1 - (blockIdx.x % nqb);
+  const size_t base = (size_t)head * N * kD;
+  const int i = qb * kRows + threadIdx.x;
+  const bool valid = i < N;
+  A qr[kD], dor[kD], g[kD];
+#pragma unroll
+  for (int d = 0; d < kD; ++d) {
+    qr[d] = valid ? widen(q[base + (size_t)i * kD + d]) : A(0);
+    dor[d] = valid ? widen(dout[base + (size_t)i * kD + d]) : A(0);
+    g[d] = 0;
+  }
+  const A li = valid ? lse[(size_t)head * N + i] : A(0);
+  const A di = valid ? delta[(size_t)head * N + i] : A(0);
+  const int kend = min(N, (qb + 1) * kRows);
+  for (int k0 = 0; k0 < kend; k0 += kTile) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < kTile * kD; e += kRows) {
+      const int r = e / kD, c = e % kD, j = k0 + r;
+      ks[r][c] = j < N ? widen(k[base + (size_t)j * kD + c]) : A(0);
+      vs[r][c] = j < N ? widen(v[base + (size_t)j * kD + c]) : A(0);
+    }
+    __syncthreads();
+    const int jn = min(kTile, kend - k0);
+    for (int jj = 0; jj < jn; ++jj) {
+      if (k0 + jj > i) break;
+      A s = 0, dp = 0;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) {
+        s += qr[d] * ks[jj][d];
+        dp += dor[d] * vs[jj][d];
+      }
+      const A p = exp_acc(s * scale - li);
+      const A dsc = p * (dp - di) * scale;
+#pragma unroll
+      for (int d = 0; d < kD; ++d) g[d] += dsc * ks[jj][d];
+    }
+  }
+  if (valid) {
+#pragma unroll
+    for (int d = 0; d < kD; ++d) dq[base + (size_t)i * kD + d] = narrow<T>(g[d]);
+  }
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64_t heads,
+                      int64_t N, double scale, hipStream_t stream, const Timers& tm) {
+  using A = acc_t<T>;
+  const int nqb = (int)((N + kRows - 1) / kRows);
+  if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
+  hipLaunchKernelGGL(fwd_rowwise<T>, dim3((unsigned)(heads * nqb)), dim3(kRows), 0, stream, q, k,
+                     v, o, (A*)lse, (int)N, nqb, (A)scale);
+  if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
+  return hipGetLastError();
+}
+
+template <typename T>
+size_t bwd_workspace_bytes(int64_t heads, int64_t N) {
+  return (size_t)heads * N * sizeof(acc_t<T>);
+}
+
+template <typename T>
+hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* dout,
+                      const void* lse, T* dq, T* dk, T* dv, void* workspace, int64_t heads,
+                      int64_t N, double scale, hipStream_t stream, const Timers& tm) {
+  using A = acc_t<T>;
+  A* delta = (A*)workspace;
+  const int64_t rows = heads * N;
+  if (hipError_t e = mark(tm.start[kTimerBwdPre], stream)) return e;
+  hipLaunchKernelGGL(bwd_delta<T>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, o,
+                     dout, delta, rows);
+  if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
+  const int nb = (int)((N + kRows - 1) / kRows);
+  if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
+  hipLaunchKernelGGL(bwd_dkdv_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kRows), 0, stream, q,
+                     k, v, dout, (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale);
+  if (hipError_t e = mark(tm.stop[kTimerBwdDkdv], stream)) return e;
+  if (hipError_t e = mark(tm.start[kTimerBwdDq], stream)) return e;
+  hipLaunchKernelGGL(bwd_dq_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kRows), 0, stream, q, k,
+                     v, dout, (const A*)lse, delta, dq, (int)N, nb, (A)scale);
+  if (hipError_t e = mark(tm.stop[kTimerBwdDq], stream)) return e;
+  return hipGetLastError();
+}
+
+#define ATTN_INSTANTIATE(T)                                                                     \
+  template hipError_t launch_fwd<T>(const T*, const T*, const T*, T*, void*, int64_t, int64_t, \
+                                    double, hipStream_t, const Timers&);                        \
+  template size_t bwd_workspace_bytes<T>(int64_t, int64_t);                                    \
+  template hipError_t launch_bwd<T>(const T*, const T*, const T*, const T*, const T*,          \
+                                    const void*, T*, T*, T*, void*, int64_t, int64_t, double,  \
+                                    hipStream_t, const Timers&);
+ATTN_INSTANTIATE(double)
+ATTN_INSTANTIATE(float)
+ATTN_INSTANTIATE(__bf16)
+
+}  // namespace attn

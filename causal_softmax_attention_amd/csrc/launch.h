@@ -1,0 +1,41 @@
+// Host-side launchers of the library's kernels.  Sizes are validated by the
+// C ABI layer (attn_api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// Caller-supplied timing events, one start/stop pair per kernel slot
+// (ATTN_TIMER_* in include/attn.h); null events are skipped.
+struct Timers {
+  hipEvent_t start[5] = {};
+  hipEvent_t stop[5] = {};
+};
+enum { kTimerFwd = 0, kTimerBwdPre = 1, kTimerBwdDkdv = 2, kTimerBwdDq = 3, kTimerNw = 4 };
+
+inline hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
+
+// Forward: o, lse of `heads` independent heads of N tokens, D = 64.
+// T is double, float or __bf16 (raw 16-bit storage); lse is double for double,
+// float otherwise.
+template <typename T>
+hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64_t heads,
+                      int64_t N, double scale, hipStream_t stream, const Timers& tm);
+
+// Backward workspace bytes and launch (dq, dk, dv from q, k, v, o, dout, lse).
+template <typename T>
+size_t bwd_workspace_bytes(int64_t heads, int64_t N);
+
+template <typename T>
+hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* dout,
+                      const void* lse, T* dq, T* dk, T* dv, void* workspace, int64_t heads,
+                      int64_t N, double scale, hipStream_t stream, const Timers& tm);
+
+hipError_t launch_nw(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,
+                     const float* sx, const float* sy, const float* sv, float denom, float* out,
+                     hipStream_t stream, const Timers& tm);
+
+}  // namespace attn

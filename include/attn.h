@@ -1,0 +1,130 @@
+/*
+ * attn.h - C ABI of the causal softmax attention library for MI355X (gfx950).
+ *
+ * The operation (pages: "Show HN: automatic deduction of FlashAttention kernel
+ * from 25 lines of SQL", neshdevtech.com, the view `attention` in its window
+ * and GROUP BY spellings, the GRADIENT statement and the NADARAYA_WATSON
+ * query):
+ *
+ *   s_ij = scale * sum_d q_id k_jd          for every pair j <= i (j > i: absent)
+ *   o_i  = sum_{j<=i} softmax_j(s_i.) v_j    an absent pair contributes nothing,
+ *                                            so an infinity in v_j reaches only
+ *                                            rows i >= j
+ *   lse_i = ln sum_{j<=i} exp(s_ij)          natural log of the scaled scores
+ *
+ * and the gradient of a loss L whose upstream gradient is dout = dL/do
+ * (for the pages' loss sum(o^2)/2, dout = o).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, contiguous, row-major [B, H, N, D] (q, k, v, o, dout,
+ *     dq, dk, dv) or [B, H, N] (lse).  Each (b, h) is one independent head.
+ *   - Every pointer is device memory owned by the caller, 16-byte aligned (4-byte
+ *     for the float columns of nw_gauss_average).  The library never
+ *     allocates, frees or synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
+ *     ATTN_OK means every launch was accepted; results are valid once the
+ *     caller has synchronised the stream.  A device fault surfaces there.
+ *   - Errors: a non-zero return; no launch has been made for ATTN_EINVAL and
+ *     ATTN_EUNSUPPORTED.  attn_last_error() returns the calling thread's last
+ *     message.  The library keeps no other state; calls from several host
+ *     threads are safe.
+ *   - Outputs must not alias inputs, except dout == o in attn_causal_bwd.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v, o, dout, dq, dk, dv.  Arithmetic: ATTN_F64 in
+ * float64 throughout; ATTN_F32 in float32; ATTN_BF16 multiplies bfloat16
+ * operands with float32 accumulation and float32 softmax.  lse is float64 for
+ * ATTN_F64 and float32 otherwise. */
+typedef enum { ATTN_F64 = 0, ATTN_F32 = 1, ATTN_BF16 = 2 } attn_dtype_t;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,       /* null pointer, size < 1, bad scale/denominator, short workspace */
+  ATTN_EUNSUPPORTED = 2, /* a valid request this build does not implement (D != 64) */
+  ATTN_EHIP = 3          /* the HIP runtime rejected a launch */
+};
+
+/* Forward pass (the view `attention`: scores from the join q.t >= k.t, the
+ * row max subtracted, normalised by the row sum, weighted sum of v).
+ *   dtype  attn_dtype_t of q, k, v, o
+ *   B, H   batch and heads, >= 1;  N tokens per head, >= 1;  D features, must be 64
+ *   scale  multiplier of q.k, finite and > 0 (the pages use 1/8 = 1/sqrt(64))
+ *   q, k, v  inputs [B, H, N, D];  o output [B, H, N, D];  lse output [B, H, N]
+ * Returns ATTN_OK / ATTN_EINVAL / ATTN_EUNSUPPORTED / ATTN_EHIP. */
+ATTN_API int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                    const void* q, const void* k, const void* v, void* o, void* lse,
+                    void* stream);
+
+/* Bytes of device workspace attn_causal_bwd needs for these sizes (0 on an
+ * invalid request).  The caller allocates it; its contents need not be
+ * initialised and are garbage afterwards. */
+ATTN_API size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D);
+
+/* Backward pass: dq, dk, dv of a loss with upstream gradient dout (the pages'
+ * GRADIENT statement: grad(loss, q.x), grad(loss, k.x), grad(loss, v.x) of
+ * loss = SUM(x * x) / 2, computed in one backward pass; pass dout = o for it).
+ * Scores are recomputed from q, k and the saved lse of attn_causal_fwd (same
+ * dtype, sizes and scale).
+ *   o, dout   [B, H, N, D] (may be the same pointer);  lse [B, H, N]
+ *   dq, dk, dv  outputs [B, H, N, D] in dtype
+ *   workspace   device memory of at least attn_causal_bwd_workspace_bytes()
+ * Returns ATTN_OK / ATTN_EINVAL / ATTN_EUNSUPPORTED / ATTN_EHIP. */
+ATTN_API int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                    const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const void* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Nadaraya-Watson control (the pages' NADARAYA_WATSON query): for every target
+ * p, out_p = sum_q w_pq v_q / sum_q w_pq over ALL sources q (a cross join),
+ * w_pq = exp(-((tx_p - sx_q)^2 + (ty_p - sy_q)^2) / denom).  The pages use
+ * denom = 0.25.  float32 columns (struct of arrays), float32 arithmetic with
+ * a per-target running max subtracted before exp.
+ *   n_targets, n_sources >= 1;  denom finite and > 0
+ * Returns ATTN_OK / ATTN_EINVAL / ATTN_EHIP. */
+ATTN_API int nw_gauss_average(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,
+                     const float* sx, const float* sy, const float* sv, float denom,
+                     float* out, void* stream);
+
+/* Profiling hook: timing events around one kernel.  Kernels are named by
+ * slot: ATTN_TIMER_FWD (the forward kernel), ATTN_TIMER_BWD_PRE (the
+ * backward's per-row delta kernel), ATTN_TIMER_BWD_DKDV (dK/dV), ATTN_TIMER_BWD_DQ
+ * (dQ), ATTN_TIMER_NW (the Nadaraya-Watson kernel).  While a slot is set (per
+ * host thread), each call that launches that kernel records `start` on its
+ * stream just before the launch and `stop` just after it, so hipEventElapsedTime
+ * gives the kernel's duration.  Both are hipEvent_t created by the caller; pass
+ * NULL, NULL to clear the slot.  Returns ATTN_OK, or ATTN_EINVAL for an unknown
+ * slot or when exactly one event is NULL. */
+enum {
+  ATTN_TIMER_FWD = 0,
+  ATTN_TIMER_BWD_PRE = 1,
+  ATTN_TIMER_BWD_DKDV = 2,
+  ATTN_TIMER_BWD_DQ = 3,
+  ATTN_TIMER_NW = 4,
+  ATTN_TIMER_SLOTS = 5
+};
+ATTN_API int attn_set_kernel_timer(int slot, void* start, void* stop);
+
+/* Message of the calling thread's most recent error ("" if none).  The pointer
+ * stays valid until that thread's next call into the library. */
+ATTN_API const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

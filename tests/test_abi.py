@@ -1,0 +1,141 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/attn.h declares, and rejects invalid arguments before any launch.
+No call here reaches a kernel (these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import causal_softmax_attention_amd as csa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(csa.LIB_PATH):
+        from causal_softmax_attention_amd import _build
+        _build.build()
+    return csa.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^ATTN_API\s+[\w\s\*]*?\b(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_symbols() == sorted(["attn_causal_fwd", "attn_causal_bwd",
+                                         "attn_causal_bwd_workspace_bytes", "nw_gauss_average",
+                                         "attn_set_kernel_timer", "attn_last_error"])
+
+
+def test_library_exports_every_declared_symbol(L):
+    out = subprocess.run(["nm", "-D", "--defined-only", csa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for sym in declared_symbols():
+        assert sym in exported, sym
+        assert hasattr(L, sym)
+    # nothing else leaks out of the library
+    assert exported == set(declared_symbols())
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "attn.h"\nint main(void){return ATTN_OK + ATTN_BF16;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c",
+                    str(src), "-o", str(tmp_path / "t.o")], check=True)
+
+
+P = ctypes.c_void_p(0x1000)  # a non-null, aligned dummy: never dereferenced on these paths
+
+
+def fwd(L, dtype=2, B=1, H=1, N=16, D=64, scale=0.125, q=P, k=P, v=P, o=None, lse=None):
+    o = ctypes.c_void_p(0x100000) if o is None else o
+    lse = ctypes.c_void_p(0x200000) if lse is None else lse
+    return L.attn_causal_fwd(dtype, B, H, N, D, scale, q, k, v, o, lse, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), csa.ATTN_EINVAL),
+    (dict(B=0), csa.ATTN_EINVAL),
+    (dict(H=-1), csa.ATTN_EINVAL),
+    (dict(N=0), csa.ATTN_EINVAL),
+    (dict(D=32), csa.ATTN_EUNSUPPORTED),
+    (dict(D=128), csa.ATTN_EUNSUPPORTED),
+    (dict(scale=0.0), csa.ATTN_EINVAL),
+    (dict(scale=float("nan")), csa.ATTN_EINVAL),
+    (dict(scale=float("inf")), csa.ATTN_EINVAL),
+    (dict(q=ctypes.c_void_p(0)), csa.ATTN_EINVAL),
+    (dict(lse=ctypes.c_void_p(0)), csa.ATTN_EINVAL),
+    (dict(k=ctypes.c_void_p(0x1004)), csa.ATTN_EINVAL),          # misaligned
+    (dict(o=P), csa.ATTN_EINVAL),                                 # o aliases q
+    (dict(N=1 << 25), csa.ATTN_EINVAL),
+])
+def test_fwd_rejects(L, kw, code):
+    assert fwd(L, **kw) == code
+    assert csa.attn_last_error() != ""
+
+
+def test_workspace_bytes(L):
+    for dt, acc in ((0, 8), (1, 4), (2, 4)):
+        n = L.attn_causal_bwd_workspace_bytes(dt, 2, 3, 100, 64)
+        assert n >= 2 * 3 * 100 * acc          # at least delta, one value per row
+    assert L.attn_causal_bwd_workspace_bytes(2, 1, 1, 16, 32) == 0
+    assert L.attn_causal_bwd_workspace_bytes(9, 1, 1, 16, 64) == 0
+
+
+def bwd(L, ws_bytes=None, **over):
+    a = dict(dtype=2, B=1, H=1, N=16, D=64, scale=0.125)
+    a.update({k: v for k, v in over.items() if k in a})
+    ptrs = {name: ctypes.c_void_p(0x100000 * (i + 1)) for i, name in
+            enumerate(["q", "k", "v", "o", "dout", "lse", "dq", "dk", "dv", "ws"])}
+    ptrs.update({k: v for k, v in over.items() if k in ptrs})
+    need = L.attn_causal_bwd_workspace_bytes(a["dtype"], a["B"], a["H"], a["N"], 64)
+    return L.attn_causal_bwd(a["dtype"], a["B"], a["H"], a["N"], a["D"], a["scale"],
+                             ptrs["q"], ptrs["k"], ptrs["v"], ptrs["o"], ptrs["dout"],
+                             ptrs["lse"], ptrs["dq"], ptrs["dk"], ptrs["dv"], ptrs["ws"],
+                             need if ws_bytes is None else ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), csa.ATTN_EINVAL),
+    (dict(N=0), csa.ATTN_EINVAL),
+    (dict(D=16), csa.ATTN_EUNSUPPORTED),
+    (dict(scale=-1.0), csa.ATTN_EINVAL),
+    (dict(dk=ctypes.c_void_p(0)), csa.ATTN_EINVAL),
+    (dict(ws=ctypes.c_void_p(0)), csa.ATTN_EINVAL),
+    (dict(ws_bytes=8), csa.ATTN_EINVAL),
+    (dict(dq=ctypes.c_void_p(0x100000)), csa.ATTN_EINVAL),      # dq aliases q
+    (dict(dv=ctypes.c_void_p(0x800000)), csa.ATTN_EINVAL),      # dv aliases dk
+    (dict(dq=ctypes.c_void_p(0x700008)), csa.ATTN_EINVAL),      # misaligned
+])
+def test_bwd_rejects(L, kw, code):
+    assert bwd(L, **kw) == code
+    assert csa.attn_last_error() != ""
+
+
+def test_nw_rejects(L):
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(6)]
+    call = lambda nt=8, ns=8, denom=0.25, ptrs=p: L.nw_gauss_average(
+        nt, ptrs[0], ptrs[1], ns, ptrs[2], ptrs[3], ptrs[4], denom, ptrs[5], None)
+    assert call(nt=0) == csa.ATTN_EINVAL
+    assert call(ns=0) == csa.ATTN_EINVAL
+    assert call(denom=0.0) == csa.ATTN_EINVAL
+    assert call(denom=float("inf")) == csa.ATTN_EINVAL
+    assert call(ptrs=p[:5] + [ctypes.c_void_p(0)]) == csa.ATTN_EINVAL
+    assert call(ptrs=p[:5] + [ctypes.c_void_p(0x100002)]) == csa.ATTN_EINVAL
+    assert call(ptrs=p[:5] + [p[0]]) == csa.ATTN_EINVAL     # out aliases tx
+
+
+def test_timer_hook(L):
+    assert L.attn_set_kernel_timer(0, P, None) == csa.ATTN_EINVAL
+    assert L.attn_set_kernel_timer(5, None, None) == csa.ATTN_EINVAL
+    assert L.attn_set_kernel_timer(-1, None, None) == csa.ATTN_EINVAL
+    for slot in range(5):
+        assert L.attn_set_kernel_timer(slot, None, None) == csa.ATTN_OK
+    assert csa.attn_last_error() == ""
