@@ -91,8 +91,8 @@ int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, doubl
                                   lse, heads, N, scale, s, g_tm);
       break;
     default:
-      e = attn::launch_fwd<__bf16>((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                                   (__bf16*)o, lse, heads, N, scale, s, g_tm);
+      e = attn::launch_fwd_bf16((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                                (__bf16*)o, (float*)lse, heads, N, scale, s, g_tm);
   }
   return hip_status(e, "attn_causal_fwd launch");
 }
