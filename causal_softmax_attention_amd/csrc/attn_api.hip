@@ -151,9 +151,10 @@ int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, doubl
                                   (float*)dk, (float*)dv, workspace, heads, N, scale, s, g_tm);
       break;
     default:
-      e = attn::launch_bwd<__bf16>((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                                   (const __bf16*)o, (const __bf16*)dout, lse, (__bf16*)dq,
-                                   (__bf16*)dk, (__bf16*)dv, workspace, heads, N, scale, s, g_tm);
+      e = attn::launch_bwd_bf16((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                                (const __bf16*)o, (const __bf16*)dout, (const float*)lse,
+                                (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, workspace, heads, N, scale,
+                                s, g_tm);
   }
   return hip_status(e, "attn_causal_bwd launch");
 }

@@ -61,6 +61,16 @@ struct Smem {
   __bf16 p[kWaves][kQW * kBc];  // per-wave weights, used only by the select path
 };
 
+// LDS tiles hold 64 rows of 64 bf16 (128 B = eight 16-byte chunks).  Chunk c of
+// row r is stored at chunk c ^ swz(r): eight consecutive rows then put a given
+// chunk in eight different bank groups (the 16-byte K reads of 8 lanes), and
+// four consecutive rows put a 32-byte pair of chunks in four different 32-byte
+// bank ranges (the 8-byte transposing V reads of 16 lanes).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int lds_at(int row, int col) {  // element offset of (row, col)
+  return row * kD + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t p = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, p);
@@ -150,8 +160,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int e = tid + u * kThreads;
-      *(uint4*)(&sm.k[buf][e * 8]) = kreg[u];
-      *(uint4*)(&sm.v[buf][e * 8]) = vreg[u];
+      const int off = lds_at(e >> 3, (e & 7) * 8);
+      *(uint4*)(&sm.k[buf][off]) = kreg[u];
+      *(uint4*)(&sm.v[buf][off]) = vreg[u];
       fin &= all_finite_bf16x8(vreg[u]);
     }
     return fin;
@@ -176,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         bf16x8_t kop[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
-          kop[kk] = *(const bf16x8_t*)(ks + (32 * kt + i32) * kD + 16 * kk + 8 * h);
+          kop[kk] = *(const bf16x8_t*)(ks + lds_at(32 * kt + i32, 16 * kk + 8 * h));
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           floatx16 acc = floatx16{};
@@ -271,9 +282,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
             const int col = 32 * dt + 16 * (g16 & 1) + 4 * (c16 & 3);
             const int row = 16 * c + 4 * (g16 >> 1) + (c16 >> 2);
             const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4s*)(vs + row * kD + col));
+                (lds_v4s*)(vs + lds_at(row, col)));
             const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_v4s*)(vs + (row + 8) * kD + col));
+                (lds_v4s*)(vs + lds_at(row + 8, col)));
             const bf16x8_t vop = __builtin_bit_cast(
                 bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
@@ -313,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 #pragma unroll
               for (int r2 = 0; r2 < 16; ++r2) {
                 const int d = 32 * dt + 8 * (r2 >> 2) + 4 * h + (r2 & 3);
-                oacc[dt][qt][r2] += pj * (float)vs[jj * kD + d];
+                oacc[dt][qt][r2] += pj * (float)vs[lds_at(jj, d)];
               }
           }
         }

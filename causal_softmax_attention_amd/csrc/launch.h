@@ -39,6 +39,12 @@ hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __
                            float* lse, int64_t heads, int64_t N, double scale, hipStream_t stream,
                            const Timers& tm);
 
+// bfloat16 backward on MFMA tiles (attn_bwd_bf16.hip); workspace holds delta.
+hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
+                           const __bf16* dout, const float* lse, __bf16* dq, __bf16* dk,
+                           __bf16* dv, void* workspace, int64_t heads, int64_t N, double scale,
+                           hipStream_t stream, const Timers& tm);
+
 hipError_t launch_nw(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,
                      const float* sx, const float* sy, const float* sv, float denom, float* out,
                      hipStream_t stream, const Timers& tm);

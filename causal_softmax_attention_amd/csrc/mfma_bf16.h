@@ -1,0 +1,102 @@
+// bfloat16 MFMA building blocks for gfx950 shared by the attention kernels.
+//
+// v_mfma_f32_32x32x16_bf16 computes C[32x32] += A[32x16] B[16x32].  With lane
+// l = 32 h + i (h in {0,1}, i in 0..31):
+//   A operand: lane holds A[m = i][k = 8h .. 8h+7]       (8 bf16)
+//   B operand: lane holds B[k = 8h .. 8h+7][n = i]       (8 bf16)
+//   C / D    : lane holds C[m = 8(r/4) + 4h + r%4][n = i] for r = 0..15 (float)
+// An accumulator C (M x N) is therefore usable, after rounding to bf16, as the
+// B operand of a product that contracts over its M index: register r = 8c + t
+// of the tile is contraction slot t of chunk c (16 rows), i.e. row
+// 16c + 8(t/4) + 4h + t%4.  The matching A operand (the other factor, M' x that
+// index) must present the same row order: slots 0..3 are rows 16c + 4h + 0..3,
+// slots 4..7 rows 16c + 8 + 4h + 0..3.  ds_read_b64_tr_b16 produces exactly
+// that from a row-major tile in LDS: the 16 lanes of a group each point at 4
+// consecutive elements of a 4-row x 16-column block (lane c16: row c16/4,
+// columns 4(c16%4)..+3) and lane c16 receives column c16, rows 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+namespace mfma {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+constexpr int kRowElems = 64;  // one tile row: 64 bf16 = 128 B = eight 16-byte chunks
+
+__device__ __forceinline__ floatx16 mma(bf16x8_t a, bf16x8_t b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Tiles in LDS are row-major [rows][64] bf16 with chunk c of row r stored at
+// chunk c ^ swz(r): eight consecutive rows then put one chunk in eight
+// different bank groups (16-byte row reads by 8 lanes), and four consecutive
+// rows put a 32-byte chunk pair in four different 32-byte bank ranges (the
+// 8-byte transposing reads by 16 lanes).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int lds_at(int row, int col) {
+  return row * kRowElems + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
+}
+
+// A or B operand from the 16 bytes at (row, col..col+7) of a swizzled tile.
+__device__ __forceinline__ bf16x8_t read_row8(const __bf16* tile, int row, int col) {
+  return *(const bf16x8_t*)(tile + lds_at(row, col));
+}
+
+// Operand holding, for this lane's column `col0 + i`, rows (within chunk c of
+// 16 rows) 16c + 4h + 0..3 and 16c + 8 + 4h + 0..3 of a row-major tile: the
+// partner of a bf16-packed accumulator chunk (see the header comment).
+__device__ __forceinline__ bf16x8_t read_tr(const __bf16* tile, int lane, int c, int col0) {
+  const int g16 = lane >> 4, c16 = lane & 15;
+  const int col = col0 + 16 * (g16 & 1) + 4 * (c16 & 3);
+  const int row = 16 * c + 4 * (g16 >> 1) + (c16 >> 2);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + lds_at(row, col)));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + lds_at(row + 8, col)));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2_t p = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+__device__ __forceinline__ float sum_bf16_pair(uint32_t p, float acc) {
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p), one, acc, false);
+}
+
+// B operand of chunk c (rows 16c..16c+15 of a 32-row tile: c in {0,1}) from a
+// bf16-packed accumulator tile held as 8 dwords.
+__device__ __forceinline__ bf16x8_t chunk_op(const uint32_t* packed8, int c) {
+  const uint4 w = make_uint4(packed8[4 * c + 0], packed8[4 * c + 1], packed8[4 * c + 2],
+                             packed8[4 * c + 3]);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// Row of the accumulator register r held by lane-half h (within a 32-row tile).
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+// Workgroup -> (head, block): workgroup b runs on XCD b % 8, so the blocks of
+// head x, x + 8, ... go to XCD x in turn (their shared K/V or Q/dO rows stay in
+// that XCD's L2); within a head, `last_first` chooses whether the last block or block 0
+// comes first.
+__device__ __forceinline__ bool map_block(int b, int heads, int nblk, bool last_first, int& head,
+                                          int& blk) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int hx = (heads - xcd + 7) >> 3;  // heads with head % 8 == xcd
+  if (slot >= hx * nblk) return false;
+  head = xcd + 8 * (slot / nblk);
+  blk = last_first ? nblk - 1 - slot % nblk : slot % nblk;
+  return true;
+}
+
+__device__ __forceinline__ uint4 ldg16(const __bf16* p) { return *(const uint4*)p; }
+
+}  // namespace mfma
+}  // namespace attn
