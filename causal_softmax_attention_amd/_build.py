@@ -25,6 +25,8 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-fvisibility=hidden",
+    # MFMA results in VGPRs: the softmax reads them with plain VALU instructions
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -103,7 +103,7 @@ size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t 
   switch (dtype) {
     case ATTN_F64: return attn::bwd_workspace_bytes<double>(heads, N);
     case ATTN_F32: return attn::bwd_workspace_bytes<float>(heads, N);
-    default: return attn::bwd_workspace_bytes<__bf16>(heads, N);
+    default: return attn::bwd_workspace_bytes_bf16(heads, N);
   }
 }
 

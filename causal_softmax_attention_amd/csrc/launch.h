@@ -39,7 +39,9 @@ hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __
                            float* lse, int64_t heads, int64_t N, double scale, hipStream_t stream,
                            const Timers& tm);
 
-// bfloat16 backward on MFMA tiles (attn_bwd_bf16.hip); workspace holds delta.
+// bfloat16 backward on MFMA tiles (attn_bwd_bf16.hip); the workspace holds two floats
+// per row (delta and lse * log2(e)).
+size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N);
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
                            const __bf16* dout, const float* lse, __bf16* dq, __bf16* dk,
                            __bf16* dv, void* workspace, int64_t heads, int64_t N, double scale,

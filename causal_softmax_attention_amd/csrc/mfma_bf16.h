@@ -98,5 +98,55 @@ __device__ __forceinline__ bool map_block(int b, int heads, int nblk, bool last_
 
 __device__ __forceinline__ uint4 ldg16(const __bf16* p) { return *(const uint4*)p; }
 
+// ---- asynchronous global -> LDS staging -----------------------------------
+//
+// buffer_load_dwordx4 ... lds writes lane i's 16 bytes to LDS at M0 + 16 i.
+// A buffer resource covering exactly one head makes rows past its end read
+// as zeros (no fault, no branch).  Tiles are staged with these loads two
+// tiles ahead; the wait before each barrier leaves the newest tile's loads in
+// flight (wait_vm_barrier), and the stages are distinct __shared__ objects
+// referenced statically, so the compiler can tell a read of one stage from
+// the copy still landing in another.
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Copy rows [row0, row0 + ROWS) (64 bf16 each) of the resource's head into a
+// swizzled LDS tile.  Every thread of a 256-thread workgroup issues ROWS / 32
+// loads; wave w fills the 1 KiB stretches u * 4 + w, lane l slot l of it, and
+// slot p of the tile holds row p / 8, physical chunk p % 8.
+template <int ROWS>
+__device__ __forceinline__ void tile_async(__amdgpu_buffer_rsrc_t rsrc, __bf16* tile, int row0,
+                                           int wave, int lane) {
+#pragma unroll
+  for (int u = 0; u < ROWS / 32; ++u) {
+    const int s = u * 4 + wave;
+    const int p = s * 64 + lane, row = p >> 3;
+    const int logical = (p & 7) ^ swz(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + s * 512), 16,
+                                             (row0 + row) * 128 + logical * 16, 0, 0, 0);
+  }
+}
+
+// Copy 64 floats [row0, row0 + 64) of a per-row array into LDS (one wave, one
+// 4-byte load per lane).
+__device__ __forceinline__ void rows_async(__amdgpu_buffer_rsrc_t rsrc, float* dst, int row0,
+                                           int lane) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)dst, 4, (row0 + lane) * 4, 0, 0, 0);
+}
+
+// Wait until at most N of this wave's buffer loads are in flight and all its
+// LDS accesses are done, then barrier (no release fence: the loads still in
+// flight belong to a stage nobody reads before the next barrier).
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
 }  // namespace mfma
 }  // namespace attn
