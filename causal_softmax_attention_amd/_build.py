@@ -25,14 +25,20 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-fvisibility=hidden",
-    # MFMA results in VGPRs: the softmax reads them with plain VALU instructions
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
+
+# Per-source additions.  The backward kernels (one wave per SIMD, 512
+# registers) keep MFMA results in VGPRs, where the softmax reads them with
+# plain VALU instructions; the forward (two waves per SIMD) does better with
+# its accumulators in AGPRs.
+EXTRA = {
+    "attn_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

@@ -43,6 +43,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsW = 64;               // stationary rows per wave
 constexpr int kBlk = kRowsW * kWaves;    // stationary rows per workgroup
 constexpr int kT = 64;                   // streamed rows per tile
+constexpr int kT2 = 2 * kT;              // streamed rows per LDS stage (two tiles per barrier)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Per row: delta_i = sum_d dO_id O_id and lse2_i = lse_i log2(e) (the base-2
@@ -157,10 +158,10 @@ __device__ __forceinline__ void dkdv_tile(const __bf16* qs, const __bf16* os, co
 }
 
 struct QStage {
-  __bf16 q[kT * kD];
-  __bf16 dout[kT * kD];
-  float lse2[kT];
-  float delta[kT];
+  __bf16 q[kT2 * kD];
+  __bf16 dout[kT2 * kD];
+  float lse2[kT2];
+  float delta[kT2];
 };
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
@@ -203,30 +204,36 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
     }
 
   const int qstart = kb * kBlk;  // queries before it see none of these keys
-  const int ntiles = (N - qstart + kT - 1) / kT;
+  const int ntiles = (N - qstart + kT2 - 1) / kT2;  // stages of 128 queries
   const uint32_t tbytes = (uint32_t)N * kD * 2, rbytes = (uint32_t)N * 4;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + base, tbytes), ro = head_rsrc(dout + base, tbytes);
   const __amdgpu_buffer_rsrc_t rl = head_rsrc(lse2g + rbase, rbytes), rd = head_rsrc(deltag + rbase, rbytes);
   auto issue = [&](QStage& s, int t) {
-    const int r0 = qstart + t * kT;
-    if (wave == 0) rows_async(rl, s.lse2, r0, lane);
-    if (wave == 1) rows_async(rd, s.delta, r0, lane);
-    tile_async<kT>(rq, s.q, r0, wave, lane);
-    tile_async<kT>(ro, s.dout, r0, wave, lane);
+    const int r0 = qstart + t * kT2;
+    // one 64-row half of lse2 / delta per wave, then the Q and dO rows
+    if (wave < 2) rows_async(rl, s.lse2 + 64 * wave, r0 + 64 * wave, lane);
+    else rows_async(rd, s.delta + 64 * (wave - 2), r0 + 64 * (wave - 2), lane);
+    tile_async<kT2>(rq, s.q, r0, wave, lane);
+    tile_async<kT2>(ro, s.dout, r0, wave, lane);
   };
   auto step = [&](QStage& cur, QStage& ahead, int t) {
     const bool pre = t + 2 < ntiles;
     if (pre) issue(ahead, t + 2);
-    const int q0 = qstart + t * kT;
-    if (kw < N && q0 + kT - 1 >= kw) {
-      if ((q0 < kw + kRowsW - 1) || (q0 + kT > N))
-        dkdv_tile<true>(cur.q, cur.dout, cur.lse2, cur.delta, lane, q0, kw, N, c_scale, kop, vop,
-                        dkacc, dvacc);
-      else
-        dkdv_tile<false>(cur.q, cur.dout, cur.lse2, cur.delta, lane, q0, kw, N, c_scale, kop,
-                         vop, dkacc, dvacc);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int q0 = qstart + t * kT2 + sub * kT;
+      const __bf16* qs = cur.q + sub * kT * kD;
+      const __bf16* os = cur.dout + sub * kT * kD;
+      if (kw < N && q0 + kT - 1 >= kw) {
+        if ((q0 < kw + kRowsW - 1) || (q0 + kT > N))
+          dkdv_tile<true>(qs, os, cur.lse2 + sub * kT, cur.delta + sub * kT, lane, q0, kw, N,
+                          c_scale, kop, vop, dkacc, dvacc);
+        else
+          dkdv_tile<false>(qs, os, cur.lse2 + sub * kT, cur.delta + sub * kT, lane, q0, kw, N,
+                           c_scale, kop, vop, dkacc, dvacc);
+      }
     }
-    if (pre) wait_vm_barrier<4>();
+    if (pre) wait_vm_barrier<8>();
     else wait_vm_barrier<0>();
   };
 
@@ -354,8 +361,8 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 }
 
 struct KVStage {
-  __bf16 k[kT * kD];
-  __bf16 v[kT * kD];
+  __bf16 k[kT2 * kD];
+  __bf16 v[kT2 * kD];
 };
 
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
@@ -398,24 +405,27 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
     for (int b = 0; b < 2; ++b) dqacc[a][b] = floatx16{};
 
   const int kend = min(N, qb * kBlk + kBlk);
-  const int ntiles = (kend + kT - 1) / kT;
+  const int ntiles = (kend + kT2 - 1) / kT2;
   const uint32_t tbytes = (uint32_t)N * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);
   auto issue = [&](KVStage& s, int t) {
-    tile_async<kT>(rk, s.k, t * kT, wave, lane);
-    tile_async<kT>(rv, s.v, t * kT, wave, lane);
+    tile_async<kT2>(rk, s.k, t * kT2, wave, lane);
+    tile_async<kT2>(rv, s.v, t * kT2, wave, lane);
   };
   auto step = [&](KVStage& cur, KVStage& ahead, int t) {
     const bool pre = t + 2 < ntiles;
     if (pre) issue(ahead, t + 2);
-    const int k0 = t * kT;
-    if (k0 <= wq_last) {
-      if ((k0 + kT - 1 > qw) || (k0 + kT > N))
-        dq_tile<true>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, lse2, dl, dqacc);
-      else
-        dq_tile<false>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, lse2, dl, dqacc);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int k0 = t * kT2 + sub * kT;
+      if (k0 <= wq_last) {
+        if ((k0 + kT - 1 > qw) || (k0 + kT > N))
+          dq_tile<true>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale, qop, oop, lse2, dl, dqacc);
+        else
+          dq_tile<false>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale, qop, oop, lse2, dl, dqacc);
+      }
     }
-    if (pre) wait_vm_barrier<4>();
+    if (pre) wait_vm_barrier<8>();
     else wait_vm_barrier<0>();
   };
 
