@@ -40,12 +40,11 @@ HBM_PEAK = 8000.0        # GB/s
 D = 64
 METRIC = "causal attn fwd+bwd TFLOP/s at N=4096 D=64 bf16; % of MFMA peak"
 
-# kernel slot -> (name in rocprofv3 output, source file, algorithmic flops per pair)
-KERNELS = {
-    "fwd": ("attn_fwd", 4 * D),
-    "bwd_dkdv": ("attn_bwd_dkdv", 8 * D),
-    "bwd_dq": ("attn_bwd_dq", 6 * D),
-}
+# Algorithmic flops per pair (i, j <= i) of each timed kernel: the products its
+# outputs need from its inputs.  fwd: S = Q K^T and O = P V; dK/dV pass:
+# S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dQ pass: S, dP, dQ = dS K.
+KERNEL_FLOPS_PER_PAIR = {"fwd": 4 * D, "bwd_dkdv": 8 * D, "bwd_dq": 6 * D, "bwd_pre": 0}
+COPY_BYTES = 256 << 20   # the plain device copy used to calibrate HBM byte counters
 
 
 def pairs(heads: int, n: int) -> int:
@@ -64,8 +63,11 @@ def source_sha(files) -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_for(slot: str, launches_per_kernel=1):
-    """HBM bytes per launch of `slot` from profiles/traffic.json, if current."""
+def traffic_for(slot: str):
+    """HBM bytes per launch of `slot` from profiles/traffic.json: rocprofv3
+    FETCH_SIZE + WRITE_SIZE of that kernel, each scaled by the byte count of
+    a plain copy over what the same counter read for it.  None unless the
+    kernel's sources still hash as they did when the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -224,6 +226,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy (3x), the known-size reference "
+                         "for rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this library has no multi-GPU path); "
@@ -237,6 +242,13 @@ def main():
         from causal_softmax_attention_amd import _build
         _build.build()
     csa.lib()
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     log("generating bf16_4k inputs")
     a, (q, k, v), _ = make_inputs("bf16_4k")
     B, H, N = q.shape[:3]
@@ -245,7 +257,7 @@ def main():
     flops = 14 * D * pairs(B * H, N)
     value = flops / ms / 1e9
     # dominant kernel
-    algo = {"fwd": 4 * D, "bwd_dkdv": 8 * D, "bwd_dq": 6 * D, "bwd_pre": 0}
+    algo = KERNEL_FLOPS_PER_PAIR
     dom = max((s for s in per if algo.get(s)), key=lambda s: per[s])
     kflops = algo[dom] * pairs(B * H, N)
     achieved = kflops / per[dom] / 1e9
