@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["attn_api.hip", "attn_rowwise.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "nw.hip"]
+SOURCES = ["attn_api.hip", "attn_rowwise.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip",
+           "attn_fwd_f32.hip", "nw.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

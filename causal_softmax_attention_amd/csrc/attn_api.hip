@@ -87,8 +87,8 @@ int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, doubl
                                    (double*)o, lse, heads, N, scale, s, g_tm);
       break;
     case ATTN_F32:
-      e = attn::launch_fwd<float>((const float*)q, (const float*)k, (const float*)v, (float*)o,
-                                  lse, heads, N, scale, s, g_tm);
+      e = attn::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o,
+                               (float*)lse, heads, N, scale, s, g_tm);
       break;
     default:
       e = attn::launch_fwd_bf16((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,

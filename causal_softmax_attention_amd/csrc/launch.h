@@ -34,6 +34,11 @@ hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* d
                       const void* lse, T* dq, T* dk, T* dv, void* workspace, int64_t heads,
                       int64_t N, double scale, hipStream_t stream, const Timers& tm);
 
+// float32 forward on MFMA tiles (attn_fwd_f32.hip).
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          int64_t heads, int64_t N, double scale, hipStream_t stream,
+                          const Timers& tm);
+
 // bfloat16 forward on MFMA tiles (attn_fwd_bf16.hip).
 hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o,
                            float* lse, int64_t heads, int64_t N, double scale, hipStream_t stream,

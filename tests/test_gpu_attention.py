@@ -120,6 +120,27 @@ def test_fp64_256_with_inf():
     assert_close("o (inf run)", oh, wo, TOL["f64"])
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_inf_value_several_tiles(dtype):
+    """V[150, 5] = +inf with 2 heads of 700 tokens: it reaches rows >= 150 of its
+    head, in column 5 only, and every other entry matches the oracle."""
+    B, H, N, j = 1, 2, 700, 150
+    a = inp.attention_inputs(31, B, H, N, dtype)
+    note(f"inf in V, several tiles, {dtype}")
+    q, k, v = (to_dev(getattr(a, x), dtype) for x in "qkv")
+    v[0, 1, j, 5] = float("inf")
+    o, lse = run_fwd(q, k, v, S)
+    oh, lh = to_host(o)[0, 1], to_host(lse)[0, 1]
+    assert np.isposinf(oh[j:, 5]).all()
+    assert np.isfinite(np.delete(oh, 5, axis=1)).all() and np.isfinite(oh[:j]).all()
+    vh = a.as_f64("v")[0, 1].copy()
+    vh[j, 5] = np.inf
+    wo, wl = oracle.forward_head(a.as_f64("q")[0, 1], a.as_f64("k")[0, 1], vh, S)[:2]
+    assert_close("o (inf run)", oh, wo, TOL[dtype])
+    assert_close("lse (inf run)", lh, wl, TOL[dtype])
+    _check_fwd(a, o, lse, sel=[(0, 0)])
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_page_mask_case(dtype):
     """The demo's own mask check: n = 16, +inf at v[9, 0], seed 1."""
