@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_api.hip", "attn_rowwise.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip",
-           "attn_fwd_f32.hip", "nw.hip"]
+           "attn_bwd_dq_bf16.hip", "attn_fwd_f32.hip", "nw.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -28,12 +28,12 @@ FLAGS = [
     "-munsafe-fp-atomics", "-fvisibility=hidden",
 ]
 
-# Per-source additions.  The backward kernels (one wave per SIMD, 512
-# registers) keep MFMA results in VGPRs, where the softmax reads them with
-# plain VALU instructions; the forward (two waves per SIMD) does better with
-# its accumulators in AGPRs.
+# Per-source additions.  The dQ pass (one wave per SIMD, 512 registers) keeps
+# MFMA results in VGPRs, where the softmax reads them with plain VALU
+# instructions; the dK/dV pass needs more registers than VGPRs alone hold and
+# keeps its accumulators in AGPRs.
 EXTRA = {
-    "attn_bwd_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "attn_bwd_dq_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -1,0 +1,237 @@
+// dQ of the bfloat16 causal attention backward on gfx950 MFMA: the
+// query-stationary pass (a wave owns 64 queries; K, V stream through LDS).
+// The per-row values it reads, -delta_i and -lse_i / scale, come from the
+// backward's prep kernel (attn_bwd_bf16.hip), which also documents the
+// gradient formulas (pages: "Show HN: automatic deduction of FlashAttention
+// kernel from 25 lines of SQL", the GRADIENT statement).
+#include "common.h"
+#include "launch.h"
+#include "mfma_bf16.h"
+
+namespace attn {
+namespace {
+
+using namespace mfma;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsW = 64;               // queries per wave
+constexpr int kBlk = kRowsW * kWaves;    // queries per workgroup
+constexpr int kT = 64;                   // keys per tile
+constexpr int kT2 = 2 * kT;              // keys per LDS stage (two tiles per barrier)
+
+// ---- dQ, query-stationary ---------------------------------------------------
+//
+// One key tile of the dQ pass for one wave (64 queries x 64 keys), as two
+// halves of 32 keys: the second half's S^T / dP^T MFMAs are issued before the
+// first half's exp / VALU work, and the first half's dQ MFMAs before the
+// second half's, so each wave always has independent MFMA and VALU work in
+// flight.  The score accumulators start from -lse/scale and -delta of their
+// query (one per lane), as in the dK/dV pass.  MASKED: the tile crosses the
+// wave's diagonal or the end of the sequence, so absent pairs get weight 0 (a
+// select, not a branch).
+template <bool MASKED>
+__device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[2], const floatx16 (&dp)[2],
+                                                uint32_t (&dsp)[2][8], int kt, int k0, int qw,
+                                                int N, int i32, int h, float c_scale) {
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = qw + 32 * qt + i32;
+#pragma unroll
+    for (int pr = 0; pr < 8; ++pr) {
+      float dsv[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * pr + e;
+        float p = __builtin_amdgcn_exp2f(s[qt][r] * c_scale);
+        if (MASKED) {
+          const int key = k0 + 32 * kt + acc_row(r, h);
+          p = (key > qi || key >= N) ? 0.f : p;
+        }
+        dsv[e] = p * dp[qt][r];
+      }
+      dsp[qt][pr] = pack_bf16(dsv[0], dsv[1]);
+    }
+  }
+}
+
+__device__ __forceinline__ void dq_half_scores(const __bf16* ks, const __bf16* vs, int kt,
+                                               int i32, int h, const bf16x8_t (&qop)[2][4],
+                                               const bf16x8_t (&oop)[2][4],
+                                               const float (&nls)[2], const float (&ndl)[2],
+                                               floatx16 (&s)[2], floatx16 (&dp)[2]) {
+  bf16x8_t ka[4], va[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    ka[kk] = read_row8(ks, 32 * kt + i32, 16 * kk + 8 * h);
+    va[kk] = read_row8(vs, 32 * kt + i32, 16 * kk + 8 * h);
+  }
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    floatx16 a, b;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      a[r] = nls[qt];
+      b[r] = ndl[qt];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      a = mma(ka[kk], qop[qt][kk], a);
+      b = mma(va[kk], oop[qt][kk], b);
+    }
+    s[qt] = a;
+    dp[qt] = b;
+  }
+}
+
+template <bool MASKED>
+__device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int lane, int k0,
+                                        int qw, int N, float c_scale,
+                                        const bf16x8_t (&qop)[2][4], const bf16x8_t (&oop)[2][4],
+                                        const float (&nls)[2], const float (&ndl)[2],
+                                        floatx16 (&dqacc)[2][2]) {
+  const int i32 = lane & 31, h = lane >> 5;
+  floatx16 s0[2], dp0[2], s1[2], dp1[2];
+  uint32_t dsp0[2][8], dsp1[2][8];
+  bf16x8_t ktr0[2][2], ktr1[2][2];
+  dq_half_scores(ks, vs, 0, i32, h, qop, oop, nls, ndl, s0, dp0);
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) ktr0[half][dt] = read_tr(ks, lane, half, 32 * dt);
+  dq_half_scores(ks, vs, 1, i32, h, qop, oop, nls, ndl, s1, dp1);
+  dq_half_softmax<MASKED>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale);
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt) ktr1[half][dt] = read_tr(ks, lane, 2 + half, 32 * dt);
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        dqacc[dt][qt] = mma(ktr0[half][dt], chunk_op(dsp0[qt], half), dqacc[dt][qt]);
+  dq_half_softmax<MASKED>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale);
+#pragma unroll
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        dqacc[dt][qt] = mma(ktr1[half][dt], chunk_op(dsp1[qt], half), dqacc[dt][qt]);
+}
+
+struct alignas(16) KVStage {
+  __bf16 k[kT2 * kD];
+  __bf16 v[kT2 * kD];
+};
+
+__global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ dout, const float* __restrict__ nlseg,
+    const float* __restrict__ ndeltag, __bf16* __restrict__ dq, int heads, int N, int nqb,
+    float c_scale, float scale) {
+  __shared__ KVStage st0, st1, st2;
+  int head, qb;
+  if (!map_block(blockIdx.x, heads, nqb, true, head, qb)) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
+  const int i32 = lane & 31, h = lane >> 5;
+  const size_t base = (size_t)head * N * kD;
+  const int qw = qb * kBlk + wave * kRowsW;
+  const int wq_last = min(qw + kRowsW, N) - 1;
+
+  // stationary B operands of S^T = K Q^T and dP^T = V dO^T; per-lane -lse/scale, -delta
+  bf16x8_t qop[2][4], oop[2][4];
+  float nls[2], ndl[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = qw + 32 * qt + i32;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      uint4 a = make_uint4(0, 0, 0, 0), b = a;
+      if (qi < N) {
+        a = ldg16(q + base + (size_t)qi * kD + 16 * kk + 8 * h);
+        b = ldg16(dout + base + (size_t)qi * kD + 16 * kk + 8 * h);
+      }
+      qop[qt][kk] = __builtin_bit_cast(bf16x8_t, a);
+      oop[qt][kk] = __builtin_bit_cast(bf16x8_t, b);
+    }
+    nls[qt] = qi < N ? nlseg[(size_t)head * N + qi] : 0.f;
+    ndl[qt] = qi < N ? ndeltag[(size_t)head * N + qi] : 0.f;
+  }
+  floatx16 dqacc[2][2];  // [dt][qt]: (feature x query), lane holds a query column
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) dqacc[a][b] = floatx16{};
+
+  const int kend = min(N, qb * kBlk + kBlk);
+  const int ntiles = (kend + kT2 - 1) / kT2;
+  const uint32_t tbytes = (uint32_t)N * kD * 2;
+  const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);
+  auto issue = [&](KVStage& s, int t) {
+    tile_async<kT2>(rk, s.k, t * kT2, wave, lane);
+    tile_async<kT2>(rv, s.v, t * kT2, wave, lane);
+  };
+  auto step = [&](KVStage& cur, KVStage& ahead, int t) {
+    const bool pre = t + 2 < ntiles;
+    if (pre) issue(ahead, t + 2);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int k0 = t * kT2 + sub * kT;
+      if (k0 <= wq_last) {
+        if ((k0 + kT - 1 > qw) || (k0 + kT > N))
+          dq_tile<true>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc);
+        else
+          dq_tile<false>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc);
+      }
+    }
+    if (pre) wait_vm_barrier<8>();
+    else wait_vm_barrier<0>();
+  };
+
+  issue(st0, 0);
+  if (ntiles > 1) issue(st1, 1);
+  wait_vm_barrier<0>();
+  for (int t = 0; t < ntiles; t += 3) {
+    step(st0, st2, t);
+    if (t + 1 < ntiles) step(st1, st0, t + 1);
+    if (t + 2 < ntiles) step(st2, st1, t + 2);
+  }
+
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = qw + 32 * qt + i32;
+    if (qi >= N) continue;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * dt + 8 * g + 4 * h;
+        uint2 w;
+        w.x = pack_bf16(dqacc[dt][qt][4 * g + 0] * scale, dqacc[dt][qt][4 * g + 1] * scale);
+        w.y = pack_bf16(dqacc[dt][qt][4 * g + 2] * scale, dqacc[dt][qt][4 * g + 3] * scale);
+        *(uint2*)(dq + base + (size_t)qi * kD + d) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_dq_bf16(const __bf16* q, const __bf16* k, const __bf16* v,
+                              const __bf16* dout, const float* nlse, const float* ndelta,
+                              __bf16* dq, int64_t heads, int64_t N, double scale,
+                              hipStream_t stream, const Timers& tm) {
+  const float c = (float)(scale * 1.4426950408889634);
+  const int nb = (int)((N + kBlk - 1) / kBlk);
+  const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nb);
+  if (hipError_t e = mark(tm.start[kTimerBwdDq], stream)) return e;
+  hipLaunchKernelGGL(bwd_dq_bf16, dim3(grid), dim3(kThreads), 0, stream, q, k, v, dout, nlse,
+                     ndelta, dq, (int)heads, (int)N, nb, c, (float)scale);
+  if (hipError_t e = mark(tm.stop[kTimerBwdDq], stream)) return e;
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -45,12 +45,18 @@ hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __
                            const Timers& tm);
 
 // bfloat16 backward on MFMA tiles (attn_bwd_bf16.hip); the workspace holds two floats
-// per row (delta and lse * log2(e)).
+// per row (-delta and -lse / scale).
 size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N);
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
                            const __bf16* dout, const float* lse, __bf16* dq, __bf16* dk,
                            __bf16* dv, void* workspace, int64_t heads, int64_t N, double scale,
                            hipStream_t stream, const Timers& tm);
+
+// The dQ pass alone (attn_bwd_dq_bf16.hip), from the prep kernel's per-row values.
+hipError_t launch_bwd_dq_bf16(const __bf16* q, const __bf16* k, const __bf16* v,
+                              const __bf16* dout, const float* nlse, const float* ndelta,
+                              __bf16* dq, int64_t heads, int64_t N, double scale,
+                              hipStream_t stream, const Timers& tm);
 
 hipError_t launch_nw(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,
                      const float* sx, const float* sy, const float* sv, float denom, float* out,
