@@ -1,78 +1,102 @@
-// Row-per-lane causal attention, forward and backward, for every storage type.
+// Row-per-group causal attention, forward and backward, for float64 (and the
+// float32 backward).
 //
-// One lane owns one query row (forward, dQ) or one key row (dK/dV) and walks
-// the other side's rows through LDS tiles, so every pair (i, j) with j <= i is
-// visited by exactly the lanes that own it and an absent pair (j > i) is never
-// touched (pages: "Show HN: automatic deduction of FlashAttention kernel from
-// 25 lines of SQL", the join predicate q.t >= k.t and the masks-are-absent-rows
-// check).  The forward keeps a running max and denominator per row (the
-// streaming plan the same page attributes to FlashAttention) and stores
-// lse = m + ln l for the backward.
+// A group of 8 lanes owns one query row (forward, dQ) or one key row (dK/dV):
+// lane g of the group holds features 8g .. 8g+7 of that row, partial dot
+// products are summed across the group with three lane exchanges, and the
+// group walks the other side's rows through LDS tiles.  Every pair (i, j) with
+// j <= i is visited by exactly the group that owns it and an absent pair
+// (j > i) is never touched (pages: "Show HN: automatic deduction of
+// FlashAttention kernel from 25 lines of SQL", the join predicate q.t >= k.t and
+// the masks-are-absent-rows check).  The forward keeps a running max and
+// denominator per row (the streaming plan the same page attributes to
+// FlashAttention) and stores lse = m + ln l for the backward.
 #include "common.h"
 #include "launch.h"
 
 namespace attn {
 namespace {
 
-constexpr int kRows = 64;   // rows per workgroup (one wave)
-constexpr int kTile = 32;   // rows of the streamed side per LDS tile
+constexpr int kG = 8;                    // lanes per row
+constexpr int kF = kD / kG;              // features per lane
+constexpr int kThr = 256;                // threads per workgroup
+constexpr int kRows = kThr / kG;         // rows per workgroup
+constexpr int kTile = 32;                // rows of the streamed side per LDS tile
+
+// Sum over the 8 lanes of a group (aligned groups: xor partners stay inside).
+template <typename A>
+__device__ __forceinline__ A group_sum(A x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  return x;
+}
+
+// Cooperative copy of rows [r0, r0 + kTile) of two [N][64] arrays into LDS
+// (rows past the end read as zero).
+template <typename T, typename A>
+__device__ __forceinline__ void load_tiles(A (*xs)[kD], A (*ys)[kD], const T* x, const T* y,
+                                           size_t base, int r0, int N) {
+  for (int e = threadIdx.x; e < kTile * kD; e += kThr) {
+    const int r = e / kD, c = e % kD, j = r0 + r;
+    xs[r][c] = j < N ? widen(x[base + (size_t)j * kD + c]) : A(0);
+    ys[r][c] = j < N ? widen(y[base + (size_t)j * kD + c]) : A(0);
+  }
+}
 
 template <typename T>
-__global__ __launch_bounds__(kRows) void fwd_rowwise(const T* __restrict__ q,
-                                                      const T* __restrict__ k,
-                                                      const T* __restrict__ v, T* __restrict__ o,
-                                                      acc_t<T>* __restrict__ lse, int N,
-                                                      int nqb, acc_t<T> scale) {
+__global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
+                                                     const T* __restrict__ k,
+                                                     const T* __restrict__ v, T* __restrict__ o,
+                                                     acc_t<T>* __restrict__ lse, int N, int nqb,
+                                                     acc_t<T> scale) {
   using A = acc_t<T>;
   __shared__ A ks[kTile][kD];
   __shared__ A vs[kTile][kD];
   const int head = blockIdx.x / nqb;
   const int qb = nqb - 1 - (blockIdx.x % nqb);  // longest rows first
   const size_t base = (size_t)head * N * kD;
-  const int i = qb * kRows + threadIdx.x;
+  const int g = threadIdx.x % kG, f0 = kF * g;
+  const int i = qb * kRows + threadIdx.x / kG;
   const bool valid = i < N;
 
-  A qr[kD], acc[kD];
+  A qr[kF], acc[kF];
 #pragma unroll
-  for (int d = 0; d < kD; ++d) {
-    qr[d] = valid ? widen(q[base + (size_t)i * kD + d]) : A(0);
-    acc[d] = 0;
+  for (int f = 0; f < kF; ++f) {
+    qr[f] = valid ? widen(q[base + (size_t)i * kD + f0 + f]) : A(0);
+    acc[f] = 0;
   }
   A m = neg_inf<A>(), l = 0;
   const int kend = min(N, (qb + 1) * kRows);
   for (int k0 = 0; k0 < kend; k0 += kTile) {
     __syncthreads();
-    for (int e = threadIdx.x; e < kTile * kD; e += kRows) {
-      const int r = e / kD, c = e % kD, j = k0 + r;
-      ks[r][c] = j < N ? widen(k[base + (size_t)j * kD + c]) : A(0);
-      vs[r][c] = j < N ? widen(v[base + (size_t)j * kD + c]) : A(0);
-    }
+    load_tiles(ks, vs, k, v, base, k0, N);
     __syncthreads();
     const int jn = min(kTile, kend - k0);
     for (int jj = 0; jj < jn; ++jj) {
-      if (k0 + jj > i) break;  // pairs j > i do not exist
+      if (k0 + jj > i) break;  // pairs j > i do not exist (the whole group leaves together)
       A s = 0;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) s += qr[d] * ks[jj][d];
-      s *= scale;
+      for (int f = 0; f < kF; ++f) s += qr[f] * ks[jj][f0 + f];
+      s = group_sum(s) * scale;
       if (s > m) {
         const A alpha = exp_acc(m - s);
         l *= alpha;
 #pragma unroll
-        for (int d = 0; d < kD; ++d) acc[d] *= alpha;
+        for (int f = 0; f < kF; ++f) acc[f] *= alpha;
         m = s;
       }
       const A p = exp_acc(s - m);
       l += p;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) acc[d] += p * vs[jj][d];
+      for (int f = 0; f < kF; ++f) acc[f] += p * vs[jj][f0 + f];
     }
   }
   if (valid) {
     const A inv = A(1) / l;
 #pragma unroll
-    for (int d = 0; d < kD; ++d) o[base + (size_t)i * kD + d] = narrow<T>(acc[d] * inv);
-    lse[(size_t)head * N + i] = m + log_acc(l);
+    for (int f = 0; f < kF; ++f) o[base + (size_t)i * kD + f0 + f] = narrow<T>(acc[f] * inv);
+    if (g == 0) lse[(size_t)head * N + i] = m + log_acc(l);
   }
 }
 
@@ -89,9 +113,9 @@ __global__ __launch_bounds__(256) void bwd_delta(const T* __restrict__ o, const 
   delta[r] = s;
 }
 
-// dK, dV: one lane per key j, queries i >= j streamed through LDS.
+// dK, dV: one group per key j, queries i >= j streamed through LDS.
 template <typename T>
-__global__ __launch_bounds__(kRows) void bwd_dkdv_rowwise(
+__global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
     const acc_t<T>* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int N, int nkb,
@@ -103,23 +127,20 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_rowwise(
   const int head = blockIdx.x / nkb;
   const int kb = blockIdx.x % nkb;  // low key blocks see the most queries: they come first
   const size_t base = (size_t)head * N * kD;
-  const int j = kb * kRows + threadIdx.x;
+  const int g = threadIdx.x % kG, f0 = kF * g;
+  const int j = kb * kRows + threadIdx.x / kG;
   const bool valid = j < N;
-  A kr[kD], vr[kD], gk[kD], gv[kD];
+  A kr[kF], vr[kF], gk[kF], gv[kF];
 #pragma unroll
-  for (int d = 0; d < kD; ++d) {
-    kr[d] = valid ? widen(k[base + (size_t)j * kD + d]) : A(0);
-    vr[d] = valid ? widen(v[base + (size_t)j * kD + d]) : A(0);
-    gk[d] = 0;
-    gv[d] = 0;
+  for (int f = 0; f < kF; ++f) {
+    kr[f] = valid ? widen(k[base + (size_t)j * kD + f0 + f]) : A(0);
+    vr[f] = valid ? widen(v[base + (size_t)j * kD + f0 + f]) : A(0);
+    gk[f] = 0;
+    gv[f] = 0;
   }
   for (int q0 = kb * kRows; q0 < N; q0 += kTile) {
     __syncthreads();
-    for (int e = threadIdx.x; e < kTile * kD; e += kRows) {
-      const int r = e / kD, c = e % kD, i = q0 + r;
-      qs[r][c] = i < N ? widen(q[base + (size_t)i * kD + c]) : A(0);
-      dos[r][c] = i < N ? widen(dout[base + (size_t)i * kD + c]) : A(0);
-    }
+    load_tiles(qs, dos, q, dout, base, q0, N);
     if (threadIdx.x < kTile) {
       const int i = q0 + threadIdx.x;
       ls[threadIdx.x] = i < N ? lse[(size_t)head * N + i] : A(0);
@@ -131,31 +152,33 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_rowwise(
       if (q0 + ii < j) continue;  // pair (i, j) exists only for i >= j
       A s = 0, dp = 0;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) {
-        s += qs[ii][d] * kr[d];
-        dp += dos[ii][d] * vr[d];
+      for (int f = 0; f < kF; ++f) {
+        s += qs[ii][f0 + f] * kr[f];
+        dp += dos[ii][f0 + f] * vr[f];
       }
+      s = group_sum(s);
+      dp = group_sum(dp);
       const A p = exp_acc(s * scale - ls[ii]);
       const A dsc = p * (dp - ds_[ii]) * scale;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) {
-        gv[d] += p * dos[ii][d];
-        gk[d] += dsc * qs[ii][d];
+      for (int f = 0; f < kF; ++f) {
+        gv[f] += p * dos[ii][f0 + f];
+        gk[f] += dsc * qs[ii][f0 + f];
       }
     }
   }
   if (valid) {
 #pragma unroll
-    for (int d = 0; d < kD; ++d) {
-      dk[base + (size_t)j * kD + d] = narrow<T>(gk[d]);
-      dv[base + (size_t)j * kD + d] = narrow<T>(gv[d]);
+    for (int f = 0; f < kF; ++f) {
+      dk[base + (size_t)j * kD + f0 + f] = narrow<T>(gk[f]);
+      dv[base + (size_t)j * kD + f0 + f] = narrow<T>(gv[f]);
     }
   }
 }
 
-// dQ: one lane per query i, keys j <= i streamed through LDS.
+// dQ: one group per query i, keys j <= i streamed through LDS.
 template <typename T>
-__global__ __launch_bounds__(kRows) void bwd_dq_rowwise(
+__global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
     const acc_t<T>* __restrict__ delta, T* __restrict__ dq, int N, int nqb, acc_t<T> scale) {
@@ -165,44 +188,43 @@ __global__ __launch_bounds__(kRows) void bwd_dq_rowwise(
   const int head = blockIdx.x / nqb;
   const int qb = nqb - 1 - (blockIdx.x % nqb);
   const size_t base = (size_t)head * N * kD;
-  const int i = qb * kRows + threadIdx.x;
+  const int g = threadIdx.x % kG, f0 = kF * g;
+  const int i = qb * kRows + threadIdx.x / kG;
   const bool valid = i < N;
-  A qr[kD], dor[kD], g[kD];
+  A qr[kF], dor[kF], gq[kF];
 #pragma unroll
-  for (int d = 0; d < kD; ++d) {
-    qr[d] = valid ? widen(q[base + (size_t)i * kD + d]) : A(0);
-    dor[d] = valid ? widen(dout[base + (size_t)i * kD + d]) : A(0);
-    g[d] = 0;
+  for (int f = 0; f < kF; ++f) {
+    qr[f] = valid ? widen(q[base + (size_t)i * kD + f0 + f]) : A(0);
+    dor[f] = valid ? widen(dout[base + (size_t)i * kD + f0 + f]) : A(0);
+    gq[f] = 0;
   }
   const A li = valid ? lse[(size_t)head * N + i] : A(0);
   const A di = valid ? delta[(size_t)head * N + i] : A(0);
   const int kend = min(N, (qb + 1) * kRows);
   for (int k0 = 0; k0 < kend; k0 += kTile) {
     __syncthreads();
-    for (int e = threadIdx.x; e < kTile * kD; e += kRows) {
-      const int r = e / kD, c = e % kD, j = k0 + r;
-      ks[r][c] = j < N ? widen(k[base + (size_t)j * kD + c]) : A(0);
-      vs[r][c] = j < N ? widen(v[base + (size_t)j * kD + c]) : A(0);
-    }
+    load_tiles(ks, vs, k, v, base, k0, N);
     __syncthreads();
     const int jn = min(kTile, kend - k0);
     for (int jj = 0; jj < jn; ++jj) {
       if (k0 + jj > i) break;
       A s = 0, dp = 0;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) {
-        s += qr[d] * ks[jj][d];
-        dp += dor[d] * vs[jj][d];
+      for (int f = 0; f < kF; ++f) {
+        s += qr[f] * ks[jj][f0 + f];
+        dp += dor[f] * vs[jj][f0 + f];
       }
+      s = group_sum(s);
+      dp = group_sum(dp);
       const A p = exp_acc(s * scale - li);
       const A dsc = p * (dp - di) * scale;
 #pragma unroll
-      for (int d = 0; d < kD; ++d) g[d] += dsc * ks[jj][d];
+      for (int f = 0; f < kF; ++f) gq[f] += dsc * ks[jj][f0 + f];
     }
   }
   if (valid) {
 #pragma unroll
-    for (int d = 0; d < kD; ++d) dq[base + (size_t)i * kD + d] = narrow<T>(g[d]);
+    for (int f = 0; f < kF; ++f) dq[base + (size_t)i * kD + f0 + f] = narrow<T>(gq[f]);
   }
 }
 
@@ -214,7 +236,7 @@ hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64
   using A = acc_t<T>;
   const int nqb = (int)((N + kRows - 1) / kRows);
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
-  hipLaunchKernelGGL(fwd_rowwise<T>, dim3((unsigned)(heads * nqb)), dim3(kRows), 0, stream, q, k,
+  hipLaunchKernelGGL(fwd_rowwise<T>, dim3((unsigned)(heads * nqb)), dim3(kThr), 0, stream, q, k,
                      v, o, (A*)lse, (int)N, nqb, (A)scale);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
@@ -238,11 +260,11 @@ hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* d
   if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
   const int nb = (int)((N + kRows - 1) / kRows);
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
-  hipLaunchKernelGGL(bwd_dkdv_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kRows), 0, stream, q,
+  hipLaunchKernelGGL(bwd_dkdv_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q,
                      k, v, dout, (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale);
   if (hipError_t e = mark(tm.stop[kTimerBwdDkdv], stream)) return e;
   if (hipError_t e = mark(tm.start[kTimerBwdDq], stream)) return e;
-  hipLaunchKernelGGL(bwd_dq_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kRows), 0, stream, q, k,
+  hipLaunchKernelGGL(bwd_dq_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q, k,
                      v, dout, (const A*)lse, delta, dq, (int)N, nb, (A)scale);
   if (hipError_t e = mark(tm.stop[kTimerBwdDq], stream)) return e;
   return hipGetLastError();
@@ -256,7 +278,6 @@ hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* d
                                     const void*, T*, T*, T*, void*, int64_t, int64_t, double,  \
                                     hipStream_t, const Timers&);
 ATTN_INSTANTIATE(double)
-ATTN_INSTANTIATE(float)
-ATTN_INSTANTIATE(__bf16)  // the bf16 forward itself runs in attn_fwd_bf16.hip
+ATTN_INSTANTIATE(float)  // the float32 backward (its forward runs on MFMA, attn_fwd_f32.hip)
 
 }  // namespace attn

@@ -18,9 +18,9 @@ enum { kTimerFwd = 0, kTimerBwdPre = 1, kTimerBwdDkdv = 2, kTimerBwdDq = 3, kTim
 
 inline hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
 
-// Forward: o, lse of `heads` independent heads of N tokens, D = 64.
-// T is double, float or __bf16 (raw 16-bit storage); lse is double for double,
-// float otherwise.
+// Row-per-group kernels (attn_rowwise.hip): forward and backward of `heads`
+// independent heads of N tokens, D = 64.  T is double or float; lse is double
+// for double, float otherwise.
 template <typename T>
 hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64_t heads,
                       int64_t N, double scale, hipStream_t stream, const Timers& tm);
