@@ -1,4 +1,5 @@
-"""CPU oracle (float64 NumPy) for causal softmax attention and the
+"""CPU oracle (float64 NumPy) for causal softmax attention (and the same
+attention under the full and sliding-window join predicates) and the
 Nadaraya-Watson control.
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
@@ -8,9 +9,9 @@ no code with the GPU path.
 Parity pins (what ties each function to something other than itself) live in
 ``tests/test_oracle_*.py``.  No function here is "parity unpinned".
 """
-from .attention import (DEFAULT_SCALE, backward, backward_head, forward, forward_head,
+from .attention import (DEFAULT_SCALE, MASKS, backward, backward_head, forward, forward_head,
                         forward_head_relational, loss)
 from .nw import nw_average
 
-__all__ = ["DEFAULT_SCALE", "forward", "forward_head", "forward_head_relational", "backward",
+__all__ = ["DEFAULT_SCALE", "MASKS", "forward", "forward_head", "forward_head_relational", "backward",
            "backward_head", "loss", "nw_average"]

@@ -20,6 +20,17 @@ spellings (``ATTENTION_WINDOW`` and ``ATTENTION_GROUP_BY``), the loss of the
 * lse_i    = m_i + ln z_i (natural log of the scaled scores).  The pages do not
   name this quantity; it is the per-row value a streamed backward needs.
 
+Masks.  The join predicate decides which pairs exist; the page's central claim
+is that the same fused plan follows for any softmax-weighted average over a
+join.  ``mask`` selects the predicate (every function defaults to the page's
+causal one):
+
+* ``"causal"``: q.t >= k.t, the view ``attention``;
+* ``"full"``:   no predicate, every pair exists (the plain join, as in the
+  attention query on the Show HN post's shorter page, which has no WHERE);
+* ``"window"``: q.t >= k.t AND q.t - k.t < window, a causal band of ``window``
+  keys per query (window >= 1).
+
 The scale is an argument; the pages fix it at 1/8 (= 1/sqrt(64)).  Dividing by
 8 and multiplying by 0.125 give the same float64 result, since 0.125 is a power
 of two.
@@ -50,11 +61,32 @@ import numpy as np
 DEFAULT_SCALE = 0.125
 
 
-def _present(r0: int, r1: int, ncols: int) -> np.ndarray:
-    """Boolean (r1-r0, ncols) table of the pairs that exist: key j <= query i."""
+MASKS = ("causal", "full", "window")
+
+
+def _check_mask(mask: str, window: int) -> None:
+    if mask not in MASKS:
+        raise ValueError(f"unknown mask {mask!r}")
+    if mask == "window" and window < 1:
+        raise ValueError("window must be >= 1")
+
+
+def _present(r0: int, r1: int, ncols: int, mask: str = "causal", window: int = 0) -> np.ndarray:
+    """Boolean (r1-r0, ncols) table of the pairs that exist for queries
+    r0 .. r1-1 and keys 0 .. ncols-1 under the mask's join predicate."""
     i = np.arange(r0, r1)[:, None]
     j = np.arange(ncols)[None, :]
-    return j <= i
+    if mask == "causal":
+        return j <= i
+    if mask == "full":
+        return np.ones((r1 - r0, ncols), dtype=bool)
+    return (j <= i) & (i - j < window)
+
+
+def _key_cols(r1: int, n: int, mask: str) -> int:
+    """Keys a block of queries ending at r1 can pair with: all n for the full
+    mask, keys below r1 otherwise."""
+    return n if mask == "full" else r1
 
 
 def _sum_present(weights: np.ndarray, present: np.ndarray, values: np.ndarray) -> np.ndarray:
@@ -74,10 +106,12 @@ def _sum_present(weights: np.ndarray, present: np.ndarray, values: np.ndarray) -
 
 
 def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
-                 scale: float = DEFAULT_SCALE, block: int = 256):
+                 scale: float = DEFAULT_SCALE, block: int = 256, mask: str = "causal",
+                 window: int = 0):
     """Window spelling, matrix form.  q, k, v: (N, D) float64.
 
     Returns (o, lse, m, z): o (N, D), and per-row lse, max m, denominator z."""
+    _check_mask(mask, window)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     n = q.shape[0]
     o = np.empty_like(q)
@@ -86,13 +120,14 @@ def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     z_all = np.empty(n)
     for r0 in range(0, n, block):
         r1 = min(n, r0 + block)
-        present = _present(r0, r1, r1)
-        s = (q[r0:r1] @ k[:r1].T) * scale                       # scores
+        nc = _key_cols(r1, n, mask)
+        present = _present(r0, r1, nc, mask, window)
+        s = (q[r0:r1] @ k[:nc].T) * scale                       # scores
         m = np.max(np.where(present, s, -np.inf), axis=1)       # MAX(s) OVER (PARTITION BY i)
         with np.errstate(invalid="ignore", over="ignore"):
             w = np.where(present, np.exp(s - m[:, None]), 0.0)  # exp(s - max)
         z = w.sum(axis=1)                                       # SUM(w) GROUP BY i
-        o[r0:r1] = _sum_present(w / z[:, None], present, v[:r1])  # SUM(w / z * v)
+        o[r0:r1] = _sum_present(w / z[:, None], present, v[:nc])  # SUM(w / z * v)
         lse[r0:r1] = m + np.log(z)
         m_all[r0:r1] = m
         z_all[r0:r1] = z
@@ -100,7 +135,8 @@ def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 
 def forward_head_relational(q: np.ndarray, k: np.ndarray, v: np.ndarray,
-                            scale: float = DEFAULT_SCALE, spelling: str = "group by"):
+                            scale: float = DEFAULT_SCALE, spelling: str = "group by",
+                            mask: str = "causal", window: int = 0):
     """The view as relations in long format, one row per existing (i, j) pair.
 
     ``spelling="group by"`` computes each row's max as a GROUP BY and joins it
@@ -108,9 +144,10 @@ def forward_head_relational(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     sorting the pair rows by i.  Aggregates are scatter-adds over the pair
     rows, so absent pairs are never touched.  Quadratic memory: small N only.
     Returns (o, lse)."""
+    _check_mask(mask, window)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     n, d = q.shape
-    ii, jj = np.nonzero(np.tril(np.ones((n, n), dtype=bool)))   # q JOIN k WHERE q.t >= k.t
+    ii, jj = np.nonzero(_present(0, n, n, mask, window))        # q JOIN k WHERE <predicate>
     s = np.einsum("pd,pd->p", q[ii], k[jj]) * scale               # SUM(q.x * k.x) GROUP BY q.t, k.t
     if spelling == "group by":
         row_max = np.full(n, -np.inf)
@@ -142,38 +179,41 @@ def loss(o: np.ndarray) -> float:
 
 
 def backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray | None = None,
-                  scale: float = DEFAULT_SCALE, block: int = 256, route_max: bool = False):
+                  scale: float = DEFAULT_SCALE, block: int = 256, route_max: bool = False,
+                  mask: str = "causal", window: int = 0):
     """Gradients (dq, dk, dv) of sum_{i,d} dout_id * o_id; with dout = o (the
     default) that is the gradient of loss = sum(o^2) / 2.  Closed-form chain
     rule over the naive plan, recomputing each block's full score rows."""
+    _check_mask(mask, window)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     n = q.shape[0]
     if dout is None:
-        dout = forward_head(q, k, v, scale, block)[0]
+        dout = forward_head(q, k, v, scale, block, mask, window)[0]
     dout = np.asarray(dout, dtype=np.float64)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
     for r0 in range(0, n, block):
         r1 = min(n, r0 + block)
-        present = _present(r0, r1, r1)
-        s = (q[r0:r1] @ k[:r1].T) * scale
+        nc = _key_cols(r1, n, mask)
+        present = _present(r0, r1, nc, mask, window)
+        s = (q[r0:r1] @ k[:nc].T) * scale
         masked = np.where(present, s, -np.inf)
         m = masked.max(axis=1)
         with np.errstate(invalid="ignore", over="ignore"):
             w = np.where(present, np.exp(s - m[:, None]), 0.0)
         z = w.sum(axis=1)
         p = w / z[:, None]
-        dp = np.where(present, dout[r0:r1] @ v[:r1].T, 0.0)      # dL/dP_ij = dO_i . v_j
+        dp = np.where(present, dout[r0:r1] @ v[:nc].T, 0.0)      # dL/dP_ij = dO_i . v_j
         delta = np.sum(p * dp, axis=1)
         ds = p * (dp - delta[:, None])                           # dL/ds_ij through w_ij
         if route_max:
             # m_i is itself max_j s_ij: dL/dm_i = -sum_j dS_ij goes to the argmax pair.
             arg = np.argmax(masked, axis=1)
             ds[np.arange(r1 - r0), arg] += -ds.sum(axis=1)
-        dq[r0:r1] = (ds @ k[:r1]) * scale
-        dk[:r1] += (ds.T @ q[r0:r1]) * scale
-        dv[:r1] += p.T @ dout[r0:r1]
+        dq[r0:r1] = (ds @ k[:nc]) * scale
+        dk[:nc] += (ds.T @ q[r0:r1]) * scale
+        dv[:nc] += p.T @ dout[r0:r1]
     return dq, dk, dv
 
 
@@ -186,12 +226,14 @@ def _map_heads(fn, arrays, workers):
         return jobs, list(ex.map(lambda j: fn(*(a[j[0], j[1]] for a in arrays)), jobs))
 
 
-def forward(q, k, v, scale: float = DEFAULT_SCALE, workers: int | None = None, block: int = 256):
+def forward(q, k, v, scale: float = DEFAULT_SCALE, workers: int | None = None, block: int = 256,
+            mask: str = "causal", window: int = 0):
     """[B, H, N, D] float64 -> (o [B, H, N, D], lse [B, H, N]); heads are independent."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     o = np.empty_like(q)
     lse = np.empty(q.shape[:3])
-    jobs, res = _map_heads(lambda a, b_, c: forward_head(a, b_, c, scale, block), (q, k, v), workers)
+    jobs, res = _map_heads(lambda a, b_, c: forward_head(a, b_, c, scale, block, mask, window),
+                           (q, k, v), workers)
     for (bi, hi), (oh, lh, _, _) in zip(jobs, res):
         o[bi, hi] = oh
         lse[bi, hi] = lh
@@ -199,15 +241,16 @@ def forward(q, k, v, scale: float = DEFAULT_SCALE, workers: int | None = None, b
 
 
 def backward(q, k, v, dout=None, scale: float = DEFAULT_SCALE, workers: int | None = None,
-             block: int = 256):
+             block: int = 256, mask: str = "causal", window: int = 0):
     """[B, H, N, D] float64 -> (dq, dk, dv); dout defaults to the oracle's own o."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     if dout is None:
         arrays = (q, k, v)
-        fn = lambda a, b_, c: backward_head(a, b_, c, None, scale, block)
+        fn = lambda a, b_, c: backward_head(a, b_, c, None, scale, block, mask=mask, window=window)
     else:
         arrays = (q, k, v, np.asarray(dout, dtype=np.float64))
-        fn = lambda a, b_, c, d_: backward_head(a, b_, c, d_, scale, block)
+        fn = lambda a, b_, c, d_: backward_head(a, b_, c, d_, scale, block, mask=mask,
+                                                window=window)
     out = [np.empty_like(q) for _ in range(3)]
     jobs, res = _map_heads(fn, arrays, workers)
     for (bi, hi), grads in zip(jobs, res):

@@ -2,8 +2,9 @@
 
 Written from the mathematical definitions, not from the oracle: softmax is
 exp(s) / sum exp(s) with no max subtracted (at 50 digits nothing overflows),
-sums run over j <= i only, and gradients are central finite differences of the
-loss sum(o^2)/2 with a step far below float64 resolution.
+sums run over the keys the join predicate admits (j <= i for the causal one),
+and gradients are central finite differences of the loss sum(o^2)/2 with a
+step far below float64 resolution.
 """
 from __future__ import annotations
 
@@ -17,20 +18,39 @@ def _mp(a):
     return [[mpmath.mpf(float(x)) for x in row] for row in np.asarray(a, dtype=np.float64)]
 
 
-def attention(q, k, v, scale=0.125):
-    """(o, lse) of causal softmax attention for one head, as mpf nested lists."""
+def causal(i, n):
+    """Keys of query i under q.t >= k.t."""
+    return list(range(i + 1))
+
+
+def pairs(mask="causal", window=0):
+    """The list of keys query i may see, per join predicate: causal (j <= i),
+    full (every key), window (j <= i and i - j < window)."""
+    if mask == "causal":
+        return causal
+    if mask == "full":
+        return lambda i, n: list(range(n))
+    if mask == "window":
+        return lambda i, n: list(range(max(0, i - window + 1), i + 1))
+    raise ValueError(mask)
+
+
+def attention(q, k, v, scale=0.125, keys=causal):
+    """(o, lse) of softmax attention for one head, as mpf nested lists; keys(i, n)
+    lists the keys query i sees."""
     Q, K, V = _mp(q), _mp(k), _mp(v)
-    return _attention_mp(Q, K, V, mpmath.mpf(scale))
+    return _attention_mp(Q, K, V, mpmath.mpf(scale), keys)
 
 
-def _attention_mp(Q, K, V, scale):
+def _attention_mp(Q, K, V, scale, keys=causal):
     n, d = len(Q), len(Q[0])
     o, lse = [], []
     for i in range(n):
-        e = [mpmath.exp(mpmath.fsum(Q[i][t] * K[j][t] for t in range(d)) * scale)
-             for j in range(i + 1)]
+        js = keys(i, n)
+        e = [mpmath.exp(mpmath.fsum(Q[i][t] * K[j][t] for t in range(d)) * scale) for j in js]
         z = mpmath.fsum(e)
-        o.append([mpmath.fsum(e[j] / z * V[j][t] for j in range(i + 1)) for t in range(len(V[0]))])
+        o.append([mpmath.fsum(e[a] / z * V[j][t] for a, j in enumerate(js))
+                  for t in range(len(V[0]))])
         lse.append(mpmath.log(z))
     return o, lse
 
@@ -40,12 +60,12 @@ def to_np(x):
         else np.array([float(a) for a in x])
 
 
-def loss_mp(Q, K, V, scale):
-    o, _ = _attention_mp(Q, K, V, scale)
+def loss_mp(Q, K, V, scale, keys=causal):
+    o, _ = _attention_mp(Q, K, V, scale, keys)
     return mpmath.fsum(x * x for row in o for x in row) / 2
 
 
-def grad_fd(q, k, v, scale=0.125, h="1e-20"):
+def grad_fd(q, k, v, scale=0.125, h="1e-20", keys=causal):
     """Central finite differences of loss = sum(o^2)/2 w.r.t. every q, k, v entry."""
     h = mpmath.mpf(h)
     scale = mpmath.mpf(scale)
@@ -58,9 +78,9 @@ def grad_fd(q, k, v, scale=0.125, h="1e-20"):
             for c in range(len(a[0])):
                 x0 = a[r][c]
                 a[r][c] = x0 + h
-                lp = loss_mp(*base, scale)
+                lp = loss_mp(*base, scale, keys)
                 a[r][c] = x0 - h
-                lm = loss_mp(*base, scale)
+                lm = loss_mp(*base, scale, keys)
                 a[r][c] = x0
                 g[r, c] = float((lp - lm) / (2 * h))
         grads.append(g)

@@ -279,6 +279,108 @@ def check_nw_shift(orc):
     far = orc.nw_average(np.array([500.0]), np.array([500.0]), a.sx, a.sy, a.sv, 0.25)
     assert np.isfinite(far).all() and a.sv.min() <= far[0] <= a.sv.max()
 
+# ------------------------------------------------------------------ masks --
+# The full and sliding-window join predicates: the page's claim that the plan
+# follows for any join, taken as two more predicates (no WHERE, and a causal
+# band of `window` keys).
+
+MASK_CASES = (("full", 0), ("window", 3), ("window", 1))
+
+
+def check_mask_brute_force(orc):
+    """50-digit brute force over each predicate's own pair list."""
+    for mask, window, n, d, seed in (("full", 0, 11, 64, 60), ("window", 3, 12, 64, 61),
+                                     ("window", 5, 9, 4, 62), ("full", 0, 7, 4, 63)):
+        rng = _rng(seed)
+        q, k, v = (rng.normal(size=(n, d)) for _ in range(3))
+        o, lse = orc.forward_head(q, k, v, S, block=4, mask=mask, window=window)[:2]
+        bo, bl = brute.attention(q, k, v, S, keys=brute.pairs(mask, window))
+        assert rel_err(o, brute.to_np(bo)) < 2e-14, ("o", mask, window, n, d)
+        assert rel_err(lse, brute.to_np(bl)) < 2e-14, ("lse", mask, window, n, d)
+
+
+def check_window_limits(orc):
+    """window = 1: each query sees only itself, so o_i = v_i and lse_i = s_ii;
+    a window at least N wide is the whole causal triangle."""
+    rng = _rng(64)
+    n = 40
+    q, k, v = (rng.normal(size=(n, 64)) for _ in range(3))
+    o, lse = orc.forward_head(q, k, v, S, block=9, mask="window", window=1)[:2]
+    assert np.array_equal(o, v)
+    assert rel_err(lse, np.einsum("nd,nd->n", q, k) * S) < 1e-15
+    oc, lc = orc.forward_head(q, k, v, S, block=9)[:2]
+    for w in (n, n + 5):
+        ow, lw = orc.forward_head(q, k, v, S, block=9, mask="window", window=w)[:2]
+        assert rel_err(ow, oc) < 1e-15 and rel_err(lw, lc) < 1e-15
+
+
+def check_mask_equal_scores(orc):
+    """Q = 0: every admitted pair scores 0, so o_i is the mean of the V rows the
+    predicate admits and lse_i = ln(their count)."""
+    rng = _rng(65)
+    n, w = 50, 7
+    k, v = rng.normal(size=(n, 64)), rng.normal(size=(n, 64))
+    o, lse = orc.forward_head(np.zeros((n, 64)), k, v, S, block=16, mask="full")[:2]
+    assert rel_err(o, np.tile(v.mean(axis=0), (n, 1))) < 1e-14
+    assert rel_err(lse, np.full(n, np.log(n))) < 1e-15
+    o, lse = orc.forward_head(np.zeros((n, 64)), k, v, S, block=16, mask="window", window=w)[:2]
+    want = np.array([v[max(0, i - w + 1):i + 1].mean(axis=0) for i in range(n)])
+    assert rel_err(o, want) < 1e-14
+    assert rel_err(lse, np.log(np.minimum(np.arange(1, n + 1), w))) < 1e-15
+
+
+def check_full_key_permutation(orc):
+    """With no predicate the keys are a set: permuting K and V rows together
+    leaves O and lse unchanged (under the causal predicate it does not)."""
+    rng = _rng(66)
+    n = 37
+    q, k, v = (rng.normal(size=(n, 64)) for _ in range(3))
+    perm = rng.permutation(n)
+    o, lse = orc.forward_head(q, k, v, S, block=10, mask="full")[:2]
+    o2, l2 = orc.forward_head(q, k[perm], v[perm], S, block=10, mask="full")[:2]
+    assert rel_err(o2, o) < 1e-14 and rel_err(l2, lse) < 1e-14
+    oc = orc.forward_head(q, k[perm], v[perm], S, block=10)[0]
+    assert rel_err(oc, orc.forward_head(q, k, v, S, block=10)[0]) > 1e-3
+
+
+def check_mask_spellings(orc):
+    """Matrix and relational (window and GROUP BY) forms agree under each predicate."""
+    rng = _rng(67)
+    q, k, v = (rng.normal(size=(45, 64)) for _ in range(3))
+    for mask, window in MASK_CASES:
+        o, lse = orc.forward_head(q, k, v, S, block=13, mask=mask, window=window)[:2]
+        for spelling in ("window", "group by"):
+            o2, l2 = orc.forward_head_relational(q, k, v, S, spelling, mask=mask, window=window)
+            assert rel_err(o2, o) < 1e-14 and rel_err(l2, lse) < 1e-14, (mask, window, spelling)
+
+
+def check_mask_grad_brute_fd(orc):
+    """Gradients under the full and window predicates against 50-digit central
+    differences of the brute-force forward."""
+    for mask, window, n, d, seed in (("full", 0, 5, 4, 68), ("window", 2, 6, 3, 69)):
+        rng = _rng(seed)
+        q, k, v = (rng.normal(size=(n, d)) * 1.5 for _ in range(3))
+        got = orc.backward_head(q, k, v, None, S, block=2, mask=mask, window=window)
+        want = brute.grad_fd(q, k, v, S, keys=brute.pairs(mask, window))
+        for name, g, w in zip("qkv", got, want):
+            assert rel_err(g, w) < 1e-13, ("d" + name, mask, rel_err(g, w))
+
+
+def check_mask_grad_invariants(orc):
+    """Under any predicate each row of dS sums to 0 (so sum_j dK_j = 0) and each
+    row of P sums to 1 (so sum_j dV_j = sum_i dO_i); with the full predicate
+    row 0 sees every key, so dQ_0 is not 0."""
+    rng = _rng(70)
+    n = 41
+    q, k, v = (rng.normal(size=(n, 64)) * 2 for _ in range(3))
+    for mask, window in MASK_CASES[:2]:
+        o = orc.forward_head(q, k, v, S, mask=mask, window=window)[0]
+        dq, dk, dv = orc.backward_head(q, k, v, None, S, block=10, mask=mask, window=window)
+        assert np.abs(dk.sum(axis=0)).max() < 1e-13 * n * np.abs(dk).max(), mask
+        assert rel_err(dv.sum(axis=0), o.sum(axis=0)) < 1e-13, mask
+    dq = orc.backward_head(q, k, v, None, S, block=10, mask="full")[0]
+    assert np.abs(dq[0]).max() > 1e-3 * np.abs(dq).max()
+
 
 ATTENTION_FORWARD_CHECKS = [check_brute_force, check_worked_example, check_token0,
                             check_equal_scores, check_rows_sum_to_one, check_prefix,
@@ -286,4 +388,7 @@ ATTENTION_FORWARD_CHECKS = [check_brute_force, check_worked_example, check_token
 ATTENTION_BACKWARD_CHECKS = [check_grad_brute_fd, check_grad_fd64, check_grad_invariants,
                              check_grad_n1, check_grad_q0]
 NW_CHECKS = [check_nw_brute, check_nw_special, check_nw_shift]
-ALL_CHECKS = ATTENTION_FORWARD_CHECKS + ATTENTION_BACKWARD_CHECKS + NW_CHECKS
+MASK_CHECKS = [check_mask_brute_force, check_window_limits, check_mask_equal_scores,
+               check_full_key_permutation, check_mask_spellings, check_mask_grad_brute_fd,
+               check_mask_grad_invariants]
+ALL_CHECKS = ATTENTION_FORWARD_CHECKS + ATTENTION_BACKWARD_CHECKS + NW_CHECKS + MASK_CHECKS

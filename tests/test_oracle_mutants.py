@@ -30,8 +30,8 @@ def _load(fname, edit):
 MUTANTS = {
     "diagonal dropped": ("attention.py", ("return j <= i", "return j < i", 0), "fwd"),
     "one token of lookahead": ("attention.py", ("return j <= i", "return j <= i + 1", 0), "fwd"),
-    "scores transposed": ("attention.py", ("(q[r0:r1] @ k[:r1].T)", "(k[r0:r1] @ q[:r1].T)", 0), "fwd"),
-    "scale 1/4": ("attention.py", ("@ k[:r1].T) * scale", "@ k[:r1].T) * 0.25", 0), "fwd"),
+    "scores transposed": ("attention.py", ("(q[r0:r1] @ k[:nc].T)", "(k[r0:r1] @ q[:nc].T)", 0), "fwd"),
+    "scale 1/4": ("attention.py", ("@ k[:nc].T) * scale", "@ k[:nc].T) * 0.25", 0), "fwd"),
     "lse in log2": ("attention.py", ("lse[r0:r1] = m + np.log(z)", "lse[r0:r1] = m + np.log2(z)", 0), "fwd"),
     "not normalised": ("attention.py", ("_sum_present(w / z[:, None],", "_sum_present(w,", 0), "fwd"),
     "max added": ("attention.py", ("np.exp(s - m[:, None])", "np.exp(s + m[:, None])", 0), "fwd"),
@@ -41,13 +41,23 @@ MUTANTS = {
     "group-by joined on j": ("attention.py", ("m = row_max[ii]", "m = row_max[jj]", 0), "fwd"),
     "dS sign": ("attention.py", ("ds = p * (dp - delta[:, None])", "ds = p * (dp + delta[:, None])", 0), "bwd"),
     "delta without P": ("attention.py", ("delta = np.sum(p * dp, axis=1)", "delta = np.sum(dp, axis=1)", 0), "bwd"),
-    "dQ unscaled": ("attention.py", ("dq[r0:r1] = (ds @ k[:r1]) * scale", "dq[r0:r1] = (ds @ k[:r1])", 0), "bwd"),
+    "dQ unscaled": ("attention.py", ("dq[r0:r1] = (ds @ k[:nc]) * scale", "dq[r0:r1] = (ds @ k[:nc])", 0), "bwd"),
     "dK from k": ("attention.py", ("(ds.T @ q[r0:r1])", "(ds.T @ k[r0:r1])", 0), "bwd"),
-    "dV from v": ("attention.py", ("dv[:r1] += p.T @ dout[r0:r1]", "dv[:r1] += p.T @ v[r0:r1]", 0), "bwd"),
-    "dP from k": ("attention.py", ("dout[r0:r1] @ v[:r1].T", "dout[r0:r1] @ k[:r1].T", 0), "bwd"),
-    "dS transposed in dQ": ("attention.py", ("(ds @ k[:r1])", "(ds.T[:r1 - r0, :] @ k[:r1])", 0), "bwd"),
-    "backward unmasked": ("attention.py", ("present = _present(r0, r1, r1)",
-                                           "present = np.ones((r1 - r0, r1), dtype=bool)", 1), "bwd"),
+    "dV from v": ("attention.py", ("dv[:nc] += p.T @ dout[r0:r1]", "dv[:nc] += p.T @ v[r0:r1]", 0), "bwd"),
+    "dP from k": ("attention.py", ("dout[r0:r1] @ v[:nc].T", "dout[r0:r1] @ k[:nc].T", 0), "bwd"),
+    "dS transposed in dQ": ("attention.py", ("(ds @ k[:nc])", "(ds.T[:r1 - r0, :] @ k[:nc])", 0), "bwd"),
+    "backward unmasked": ("attention.py", ("present = _present(r0, r1, nc, mask, window)",
+                                           "present = np.ones((r1 - r0, nc), dtype=bool)", 1), "bwd"),
+    "window one key wider": ("attention.py", ("(i - j < window)", "(i - j <= window)", 0), "mask"),
+    "window not causal": ("attention.py", ("return (j <= i) & (i - j < window)",
+                                           "return np.abs(i - j) < window", 0), "mask"),
+    "full keeps the causal predicate": ("attention.py",
+                                        ("return np.ones((r1 - r0, ncols), dtype=bool)",
+                                         "return np.broadcast_to(j <= i, (r1 - r0, ncols))", 0),
+                                        "mask"),
+    "full sees only earlier blocks' keys": ("attention.py",
+                                            ('return n if mask == "full" else r1', "return r1", 0),
+                                            "mask"),
     "bandwidth 2h^2": ("nw.py", ("/ denom", "/ (2 * denom)", 0), "nw"),
     "y against x": ("nw.py", ("(ty[r0:r1, None] - sy[None, :])", "(ty[r0:r1, None] - sx[None, :])", 0), "nw"),
     "mean of weights": ("nw.py", ("(w @ sv) / w.sum(axis=1)", "(w @ sv) / w.shape[1]", 0), "nw"),
@@ -56,7 +66,8 @@ MUTANTS = {
 
 GROUPS = {"fwd": oracle_pins.ATTENTION_FORWARD_CHECKS,
           "bwd": oracle_pins.ATTENTION_BACKWARD_CHECKS,
-          "nw": oracle_pins.NW_CHECKS}
+          "nw": oracle_pins.NW_CHECKS,
+          "mask": oracle_pins.MASK_CHECKS}
 
 
 @pytest.mark.parametrize("name", list(MUTANTS))
