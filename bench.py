@@ -94,8 +94,11 @@ def make_inputs(name):
     return a, [dev(getattr(a, x)) for x in "qkv"], dt
 
 
-def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True):
-    """Run `steps` timed steps; returns (ms_per_step, {slot: mean ms}, outputs)."""
+def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask="causal",
+                   window=0):
+    """Run `steps` timed steps; returns (ms_per_step, {slot: mean ms}, outputs).
+    The causal predicate goes through attn_causal_fwd / _bwd, others through
+    attn_fwd / attn_bwd."""
     import torch
 
     import causal_softmax_attention_amd as csa
@@ -110,9 +113,15 @@ def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True):
                      dtype=torch.uint8, device=q.device)
 
     def step():
-        csa.attn_causal_fwd(q, k, v, 0.125, o=o, lse=lse)
-        if with_bwd:
-            csa.attn_causal_bwd(q, k, v, o, o, lse, 0.125, dq=dq, dk=dk, dv=dv, workspace=ws)
+        if mask == "causal":
+            csa.attn_causal_fwd(q, k, v, 0.125, o=o, lse=lse)
+            if with_bwd:
+                csa.attn_causal_bwd(q, k, v, o, o, lse, 0.125, dq=dq, dk=dk, dv=dv, workspace=ws)
+        else:
+            csa.attn_fwd(q, k, v, 0.125, mask, window, o=o, lse=lse)
+            if with_bwd:
+                csa.attn_bwd(q, k, v, o, o, lse, 0.125, mask, window, dq=dq, dk=dk, dv=dv,
+                             workspace=ws)
 
     for _ in range(warmup):
         step()
@@ -197,6 +206,19 @@ def secondary(steps):
     out["bf16_32k_fwd_bwd"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
                                "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
                                "kernels_ms": per}
+    del q, k, v
+    # the other join predicates on the same 8 x 32 x 4096 bf16 inputs; flops
+    # count each predicate's own pairs (N^2 per head for the full one)
+    a, (q, k, v), _ = make_inputs("bf16_4k")
+    B_, H_, N_ = q.shape[:3]
+    for mask, window, key in (("full", 0, "bf16_4k_full_fwd_bwd"),
+                              ("window", 512, "bf16_4k_window512_fwd_bwd")):
+        ms, _, per, _ = time_attention(q, k, v, max(2, steps // 2), 1, mask=mask, window=window)
+        npairs = B_ * H_ * (N_ * N_ if mask == "full" else
+                            sum(min(i + 1, window) for i in range(N_)))
+        fl = 14 * D * npairs
+        out[key] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
+                    "pairs": npairs, "kernels_ms": per}
     del q, k, v
     a, (q, k, v), _ = make_inputs("fp64_256")
     ms, _, per, _ = time_attention(q, k, v, steps, 2)

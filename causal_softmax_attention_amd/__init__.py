@@ -13,6 +13,8 @@ import ctypes
 import os
 
 ATTN_F64, ATTN_F32, ATTN_BF16 = 0, 1, 2
+ATTN_MASK_CAUSAL, ATTN_MASK_FULL, ATTN_MASK_WINDOW = 0, 1, 2
+MASKS = {"causal": ATTN_MASK_CAUSAL, "full": ATTN_MASK_FULL, "window": ATTN_MASK_WINDOW}
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 DEFAULT_SCALE = 0.125
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
@@ -43,6 +45,14 @@ def lib() -> ctypes.CDLL:
         L.attn_causal_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
                                       vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_causal_bwd.restype = ctypes.c_int
+        L.attn_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
+                               i64, vp, vp, vp, vp, vp, vp]
+        L.attn_fwd.restype = ctypes.c_int
+        L.attn_bwd_workspace_bytes.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+        L.attn_bwd_workspace_bytes.restype = sz
+        L.attn_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
+                               i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.attn_bwd.restype = ctypes.c_int
         L.nw_gauss_average.argtypes = [i64, vp, vp, i64, vp, vp, vp, ctypes.c_float, vp, vp]
         L.nw_gauss_average.restype = ctypes.c_int
         L.attn_set_kernel_timer.argtypes = [ctypes.c_int, vp, vp]
@@ -86,8 +96,13 @@ def _bhnd(t, name):
     return t.shape
 
 
-def attn_causal_fwd(q, k, v, scale: float = DEFAULT_SCALE, o=None, lse=None, stream=None):
-    """Forward pass; returns (o, lse).  q, k, v: [B, H, N, 64] float64/float32/bfloat16."""
+def _mask_code(mask) -> int:
+    if mask not in MASKS:
+        raise ValueError(f"mask must be one of {sorted(MASKS)}")
+    return MASKS[mask]
+
+
+def _fwd_args(q, k, v, o, lse):
     import torch
     B, H, N, D = _bhnd(q, "q")
     for name, t in (("k", k), ("v", v)):
@@ -98,8 +113,24 @@ def attn_causal_fwd(q, k, v, scale: float = DEFAULT_SCALE, o=None, lse=None, str
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float64 if q.dtype == torch.float64 else torch.float32,
                           device=q.device)
+    return (B, H, N, D), o, lse
+
+
+def attn_causal_fwd(q, k, v, scale: float = DEFAULT_SCALE, o=None, lse=None, stream=None):
+    """Forward pass; returns (o, lse).  q, k, v: [B, H, N, 64] float64/float32/bfloat16."""
+    (B, H, N, D), o, lse = _fwd_args(q, k, v, o, lse)
     _check(lib().attn_causal_fwd(_dtype_code(q), B, H, N, D, float(scale), _ptr(q), _ptr(k),
                                  _ptr(v), _ptr(o), _ptr(lse), _stream(q, stream)))
+    return o, lse
+
+
+def attn_fwd(q, k, v, scale: float = DEFAULT_SCALE, mask: str = "causal", window: int = 0,
+             o=None, lse=None, stream=None):
+    """Forward pass under a join predicate ("causal", "full" or "window" of
+    `window` keys); returns (o, lse)."""
+    (B, H, N, D), o, lse = _fwd_args(q, k, v, o, lse)
+    _check(lib().attn_fwd(_dtype_code(q), B, H, N, D, float(scale), _mask_code(mask), int(window),
+                          _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q, stream)))
     return o, lse
 
 
@@ -107,9 +138,7 @@ def attn_causal_bwd_workspace_bytes(dtype_code: int, B: int, H: int, N: int, D: 
     return int(lib().attn_causal_bwd_workspace_bytes(dtype_code, B, H, N, D))
 
 
-def attn_causal_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, dq=None, dk=None,
-                    dv=None, workspace=None, stream=None):
-    """Backward pass; returns (dq, dk, dv).  Pass dout = o for the loss sum(o^2)/2."""
+def _bwd_args(q, k, v, o, dout, dq, dk, dv, workspace):
     import torch
     B, H, N, D = _bhnd(q, "q")
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
@@ -122,10 +151,31 @@ def attn_causal_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, dq=None
     need = attn_causal_bwd_workspace_bytes(code, B, H, N, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    return (code, B, H, N, D), dq, dk, dv, workspace
+
+
+def attn_causal_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, dq=None, dk=None,
+                    dv=None, workspace=None, stream=None):
+    """Backward pass; returns (dq, dk, dv).  Pass dout = o for the loss sum(o^2)/2."""
+    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, dout, dq, dk, dv, workspace)
     _check(lib().attn_causal_bwd(code, B, H, N, D, float(scale), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                 _stream(q, stream)))
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(q, stream)))
+    return dq, dk, dv
+
+
+def attn_bwd_workspace_bytes(dtype_code: int, B: int, H: int, N: int, D: int = 64) -> int:
+    return int(lib().attn_bwd_workspace_bytes(dtype_code, B, H, N, D))
+
+
+def attn_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, mask: str = "causal",
+             window: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward pass under a join predicate (as attn_fwd); returns (dq, dk, dv)."""
+    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, dout, dq, dk, dv, workspace)
+    _check(lib().attn_bwd(code, B, H, N, D, float(scale), _mask_code(mask), int(window), _ptr(q),
+                          _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
+                          _stream(q, stream)))
     return dq, dk, dv
 
 
@@ -157,6 +207,7 @@ def attn_set_kernel_timer(slot: int, start, stop):
     _check(lib().attn_set_kernel_timer(slot, h(start), h(stop)))
 
 
-__all__ = ["attn_causal_fwd", "attn_causal_bwd", "attn_causal_bwd_workspace_bytes",
+__all__ = ["attn_causal_fwd", "attn_causal_bwd", "attn_causal_bwd_workspace_bytes", "attn_fwd",
+           "attn_bwd", "attn_bwd_workspace_bytes", "MASKS",
            "nw_gauss_average", "attn_set_kernel_timer", "attn_last_error", "lib", "AttnError",
            "ATTN_F64", "ATTN_F32", "ATTN_BF16"]

@@ -60,14 +60,29 @@ int check_sizes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double sc
   return ATTN_OK;
 }
 
+// The join predicate of a mask kind; a window at least N wide is the causal one.
+int make_mask(int mask, int64_t window, int64_t N, attn::Mask& mk) {
+  switch (mask) {
+    case ATTN_MASK_CAUSAL: mk = attn::Mask{1, 0}; return ATTN_OK;
+    case ATTN_MASK_FULL: mk = attn::Mask{0, 0}; return ATTN_OK;
+    case ATTN_MASK_WINDOW:
+      if (window < 1) return fail(ATTN_EINVAL, "window must be >= 1 (got %lld)", (long long)window);
+      mk = attn::Mask{1, window >= N ? 0 : (int)window};
+      return ATTN_OK;
+    default: return fail(ATTN_EINVAL, "unknown mask kind %d", mask);
+  }
+}
+
 }  // namespace
 
 extern "C" {
 
-int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                    const void* q, const void* k, const void* v, void* o, void* lse,
-                    void* stream) {
+int attn_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+             int64_t window, const void* q, const void* k, const void* v, void* o, void* lse,
+             void* stream) {
   if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
+  attn::Mask mk;
+  if (int rc = make_mask(mask, window, N, mk)) return rc;
   if (!q || !k || !v || !o || !lse) return fail(ATTN_EINVAL, "null pointer argument");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return fail(ATTN_EINVAL, "pointers must be 16-byte aligned");
@@ -84,17 +99,23 @@ int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, doubl
   switch (dtype) {
     case ATTN_F64:
       e = attn::launch_fwd<double>((const double*)q, (const double*)k, (const double*)v,
-                                   (double*)o, lse, heads, N, scale, s, g_tm);
+                                   (double*)o, lse, heads, N, scale, mk, s, g_tm);
       break;
     case ATTN_F32:
       e = attn::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o,
-                               (float*)lse, heads, N, scale, s, g_tm);
+                               (float*)lse, heads, N, scale, mk, s, g_tm);
       break;
     default:
       e = attn::launch_fwd_bf16((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                                (__bf16*)o, (float*)lse, heads, N, scale, s, g_tm);
+                                (__bf16*)o, (float*)lse, heads, N, scale, mk, s, g_tm);
   }
-  return hip_status(e, "attn_causal_fwd launch");
+  return hip_status(e, "attn_fwd launch");
+}
+
+int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                    const void* q, const void* k, const void* v, void* o, void* lse,
+                    void* stream) {
+  return attn_fwd(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, q, k, v, o, lse, stream);
 }
 
 size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
@@ -107,11 +128,17 @@ size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t 
   }
 }
 
-int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                    const void* q, const void* k, const void* v, const void* o,
-                    const void* dout, const void* lse, void* dq, void* dk, void* dv,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+size_t attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
+  return attn_causal_bwd_workspace_bytes(dtype, B, H, N, D);
+}
+
+int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+             int64_t window, const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const void* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, void* stream) {
   if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
+  attn::Mask mk;
+  if (int rc = make_mask(mask, window, N, mk)) return rc;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
     return fail(ATTN_EINVAL, "null pointer argument");
   const void* all[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
@@ -143,20 +170,30 @@ int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, doubl
     case ATTN_F64:
       e = attn::launch_bwd<double>((const double*)q, (const double*)k, (const double*)v,
                                    (const double*)o, (const double*)dout, lse, (double*)dq,
-                                   (double*)dk, (double*)dv, workspace, heads, N, scale, s, g_tm);
+                                   (double*)dk, (double*)dv, workspace, heads, N, scale, mk, s,
+                                   g_tm);
       break;
     case ATTN_F32:
       e = attn::launch_bwd<float>((const float*)q, (const float*)k, (const float*)v,
                                   (const float*)o, (const float*)dout, lse, (float*)dq,
-                                  (float*)dk, (float*)dv, workspace, heads, N, scale, s, g_tm);
+                                  (float*)dk, (float*)dv, workspace, heads, N, scale, mk, s,
+                                  g_tm);
       break;
     default:
       e = attn::launch_bwd_bf16((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                                 (const __bf16*)o, (const __bf16*)dout, (const float*)lse,
                                 (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, workspace, heads, N, scale,
-                                s, g_tm);
+                                mk, s, g_tm);
   }
-  return hip_status(e, "attn_causal_bwd launch");
+  return hip_status(e, "attn_bwd launch");
+}
+
+int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                    const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const void* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_bwd(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, q, k, v, o, dout, lse, dq, dk,
+                  dv, workspace, workspace_bytes, stream);
 }
 
 int nw_gauss_average(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,

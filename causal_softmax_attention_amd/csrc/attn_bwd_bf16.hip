@@ -144,13 +144,15 @@ __device__ __forceinline__ void dkdv_scores(const QStage& st, int row0, int lane
   }
 }
 
-// B: packed bf16 P and dS of one half.  MASKED: pairs with key > query get
-// weight 0 (a select).  Queries past the end need no mask: their Q and dO rows
-// read as zeros, so their dS is 0 and their P multiplies a zero dO row.
+// B: packed bf16 P and dS of one half.  MASKED: absent pairs (key > query
+// under the causal predicate, query - key >= band under a window) get weight 0
+// (a select).  Queries past the end need no mask: their Q and dO rows read as
+// zeros, so their dS is 0 and their P multiplies a zero dO row.
 template <bool MASKED>
 __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[2], const floatx16 (&dp)[2],
                                              uint32_t (&pp)[2][8], uint32_t (&dsp)[2][8],
-                                             int qrow0, int kw, int lane, float c_scale) {
+                                             int qrow0, int kw, int lane, float c_scale,
+                                             int causal, int band) {
   const int i32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
@@ -162,7 +164,10 @@ __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[2], const float
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * pr + e;
         float p = __builtin_amdgcn_exp2f(s[kt][r] * c_scale);
-        if (MASKED) p = key > qrow0 + acc_row(r, h) ? 0.f : p;
+        if (MASKED) {
+          const int qi = qrow0 + acc_row(r, h);
+          p = (causal && key > qi) || (band && qi - key >= band) ? 0.f : p;
+        }
         pv[e] = p;
         dsv[e] = p * dp[kt][r];
       }
@@ -195,13 +200,13 @@ __device__ __forceinline__ void dkdv_accum(const QStage& st, int row0, int lane,
 // is qrow0, C(n-1) from (sc, rc).  SKIP_C: there is no half n-1.
 template <bool MASKED, bool SKIP_C>
 __device__ __forceinline__ void dkdv_step(const QStage& sa, int ra, const QStage& sc, int rc,
-                                          int qrow0, int kw, int lane, float c_scale,
-                                          const bf16x8_t (&kop)[2][4],
+                                          int qrow0, int kw, int lane, float c_scale, int causal,
+                                          int band, const bf16x8_t (&kop)[2][4],
                                           const bf16x8_t (&vop)[2][4], DkdvPipe& pipe,
                                           floatx16 (&dkacc)[2][2], floatx16 (&dvacc)[2][2]) {
   uint32_t pp[2][8], dsp[2][8];
   if (!SKIP_C) dkdv_accum(sc, rc, lane, pipe.pp, pipe.dsp, dkacc, dvacc);
-  dkdv_softmax<MASKED>(pipe.s, pipe.dp, pp, dsp, qrow0, kw, lane, c_scale);
+  dkdv_softmax<MASKED>(pipe.s, pipe.dp, pp, dsp, qrow0, kw, lane, c_scale, causal, band);
   dkdv_scores(sa, ra, lane, kop, vop, pipe.s, pipe.dp);
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt)
@@ -213,11 +218,15 @@ __device__ __forceinline__ void dkdv_step(const QStage& sa, int ra, const QStage
   __builtin_amdgcn_sched_barrier(0);  // keep each step's schedule to itself
 }
 
+// BANDED: a window of band keys; every stage then takes the masked body.
+// Without it the predicate is causal (causal = 1) or absent (causal = 0).
+template <bool BANDED>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ nlseg,
     const float* __restrict__ ndeltag, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-    int heads, int N, int nkb, float c_scale, float scale) {
+    int heads, int N, int nkb, float c_scale, float scale, int causal, int band_arg) {
+  const int band = BANDED ? band_arg : 0;
   __shared__ QStage st0, st1, st2;
   int head, kb;
   if (!map_block(blockIdx.x, heads, nkb, false, head, kb)) return;
@@ -253,8 +262,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
       dvacc[a][b] = floatx16{};
     }
 
-  const int qstart = kb * kBlk;  // queries before it see none of these keys
-  const int nst = (N - qstart + kT2 - 1) / kT2;  // stages of 128 queries
+  // queries that see these keys: from the block's first key (causal) or 0, to
+  // the last key's window end or N
+  const int qstart = causal ? kb * kBlk : 0;
+  const int qend = band ? min(N, kb * kBlk + kBlk - 1 + band) : N;
+  const int nst = (qend - qstart + kT2 - 1) / kT2;  // stages of 128 queries
   const uint32_t tbytes = (uint32_t)N * kD * 2, rbytes = (uint32_t)N * 4;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + base, tbytes), ro = head_rsrc(dout + base, tbytes);
   const __amdgpu_buffer_rsrc_t rl = head_rsrc(nlseg + rbase, rbytes), rd = head_rsrc(ndeltag + rbase, rbytes);
@@ -270,13 +282,20 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
   auto stage = [&](auto masked, auto first, QStage& cur, QStage& nxt, QStage& prv, int s) {
     constexpr bool M = decltype(masked)::value, F = decltype(first)::value;
     const int q0 = qstart + s * kT2;
-    dkdv_step<M, F>(cur, 32, prv, 96, q0, kw, lane, c_scale, kop, vop, pipe, dkacc, dvacc);
+    dkdv_step<M, F>(cur, 32, prv, 96, q0, kw, lane, c_scale, causal, band, kop, vop, pipe,
+                    dkacc, dvacc);
     wait_vm_barrier<0>();  // stage s + 1 has landed; every wave is done with prv
     if (s + 2 < nst) issue(prv, s + 2);
-    dkdv_step<M, false>(cur, 64, cur, 0, q0 + 32, kw, lane, c_scale, kop, vop, pipe, dkacc, dvacc);
-    dkdv_step<M, false>(cur, 96, cur, 32, q0 + 64, kw, lane, c_scale, kop, vop, pipe, dkacc, dvacc);
-    dkdv_step<M, false>(nxt, 0, cur, 64, q0 + 96, kw, lane, c_scale, kop, vop, pipe, dkacc, dvacc);
+    dkdv_step<M, false>(cur, 64, cur, 0, q0 + 32, kw, lane, c_scale, causal, band, kop, vop,
+                        pipe, dkacc, dvacc);
+    dkdv_step<M, false>(cur, 96, cur, 32, q0 + 64, kw, lane, c_scale, causal, band, kop, vop,
+                        pipe, dkacc, dvacc);
+    dkdv_step<M, false>(nxt, 0, cur, 64, q0 + 96, kw, lane, c_scale, causal, band, kop, vop,
+                        pipe, dkacc, dvacc);
   };
+  // stages 0 and 1 hold the block's diagonal (masked body); later stages lie
+  // wholly after every key of the block, so only a window masks them
+  using LM = std::integral_constant<bool, BANDED>;
   using T = std::true_type;
   using Fl = std::false_type;
 
@@ -287,9 +306,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
   stage(T{}, T{}, st0, st1, st2, 0);
   if (nst > 1) stage(T{}, Fl{}, st1, st2, st0, 1);
   for (int s = 2; s < nst; s += 3) {
-    stage(Fl{}, Fl{}, st2, st0, st1, s);
-    if (s + 1 < nst) stage(Fl{}, Fl{}, st0, st1, st2, s + 1);
-    if (s + 2 < nst) stage(Fl{}, Fl{}, st1, st2, st0, s + 2);
+    stage(LM{}, Fl{}, st2, st0, st1, s);
+    if (s + 1 < nst) stage(LM{}, Fl{}, st0, st1, st2, s + 1);
+    if (s + 2 < nst) stage(LM{}, Fl{}, st1, st2, st0, s + 2);
   }
   // C of the last half (rows 96.. of the last stage)
   {
@@ -328,7 +347,7 @@ size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N) {
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
                            const __bf16* dout, const float* lse, __bf16* dq, __bf16* dk,
                            __bf16* dv, void* workspace, int64_t heads, int64_t N, double scale,
-                           hipStream_t stream, const Timers& tm) {
+                           const Mask& mk, hipStream_t stream, const Timers& tm) {
   const int64_t rows = heads * N;
   float* ndelta = (float*)workspace;
   float* nlse = ndelta + rows;
@@ -340,11 +359,12 @@ hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, co
                      dout, lse, ndelta, nlse, (float)(1.0 / scale), rows);
   if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
-  hipLaunchKernelGGL(bwd_dkdv_bf16, dim3(grid), dim3(kThreads), 0, stream, q, k, v, dout, nlse,
-                     ndelta, dk, dv, (int)heads, (int)N, nb, c, (float)scale);
+  auto kern = mk.band > 0 ? bwd_dkdv_bf16<true> : bwd_dkdv_bf16<false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, dout, nlse, ndelta, dk,
+                     dv, (int)heads, (int)N, nb, c, (float)scale, mk.causal, mk.band);
   if (hipError_t e = mark(tm.stop[kTimerBwdDkdv], stream)) return e;
   if (hipError_t e = hipGetLastError()) return e;
-  return launch_bwd_dq_bf16(q, k, v, dout, nlse, ndelta, dq, heads, N, scale, stream, tm);
+  return launch_bwd_dq_bf16(q, k, v, dout, nlse, ndelta, dq, heads, N, scale, mk, stream, tm);
 }
 
 }  // namespace attn

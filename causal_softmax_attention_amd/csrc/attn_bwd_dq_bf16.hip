@@ -27,13 +27,14 @@ constexpr int kT2 = 2 * kT;              // keys per LDS stage (two tiles per ba
 // first half's exp / VALU work, and the first half's dQ MFMAs before the
 // second half's, so each wave always has independent MFMA and VALU work in
 // flight.  The score accumulators start from -lse/scale and -delta of their
-// query (one per lane), as in the dK/dV pass.  MASKED: the tile crosses the
-// wave's diagonal or the end of the sequence, so absent pairs get weight 0 (a
-// select, not a branch).
+// query (one per lane), as in the dK/dV pass.  MASKED: the tile holds absent
+// pairs (past the wave's diagonal or a window's start, or past the end of the
+// sequence), which get weight 0 (a select, not a branch).
 template <bool MASKED>
 __device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[2], const floatx16 (&dp)[2],
                                                 uint32_t (&dsp)[2][8], int kt, int k0, int qw,
-                                                int N, int i32, int h, float c_scale) {
+                                                int N, int i32, int h, float c_scale, int causal,
+                                                int band) {
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int qi = qw + 32 * qt + i32;
@@ -46,7 +47,7 @@ __device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[2], const fl
         float p = __builtin_amdgcn_exp2f(s[qt][r] * c_scale);
         if (MASKED) {
           const int key = k0 + 32 * kt + acc_row(r, h);
-          p = (key > qi || key >= N) ? 0.f : p;
+          p = (key >= N || (causal && key > qi) || (band && qi - key >= band)) ? 0.f : p;
         }
         dsv[e] = p * dp[qt][r];
       }
@@ -89,7 +90,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
                                         int qw, int N, float c_scale,
                                         const bf16x8_t (&qop)[2][4], const bf16x8_t (&oop)[2][4],
                                         const float (&nls)[2], const float (&ndl)[2],
-                                        floatx16 (&dqacc)[2][2]) {
+                                        floatx16 (&dqacc)[2][2], int causal, int band) {
   const int i32 = lane & 31, h = lane >> 5;
   floatx16 s0[2], dp0[2], s1[2], dp1[2];
   uint32_t dsp0[2][8], dsp1[2][8];
@@ -100,7 +101,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) ktr0[half][dt] = read_tr(ks, lane, half, 32 * dt);
   dq_half_scores(ks, vs, 1, i32, h, qop, oop, nls, ndl, s1, dp1);
-  dq_half_softmax<MASKED>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale);
+  dq_half_softmax<MASKED>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale, causal, band);
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -112,7 +113,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
         dqacc[dt][qt] = mma(ktr0[half][dt], chunk_op(dsp0[qt], half), dqacc[dt][qt]);
-  dq_half_softmax<MASKED>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale);
+  dq_half_softmax<MASKED>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale, causal, band);
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -127,11 +128,15 @@ struct alignas(16) KVStage {
   __bf16 v[kT2 * kD];
 };
 
+// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does.
+template <bool CAUSAL, bool BANDED>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ nlseg,
     const float* __restrict__ ndeltag, __bf16* __restrict__ dq, int heads, int N, int nqb,
-    float c_scale, float scale) {
+    float c_scale, float scale, int band_arg) {
+  constexpr int causal = CAUSAL;
+  const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
   int head, qb;
   if (!map_block(blockIdx.x, heads, nqb, true, head, qb)) return;
@@ -167,8 +172,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
 #pragma unroll
     for (int b = 0; b < 2; ++b) dqacc[a][b] = floatx16{};
 
-  const int kend = min(N, qb * kBlk + kBlk);
+  // keys of the workgroup's queries: stages t0 .. ntiles-1 of 128 keys
+  const int t0 = band ? max(0, qb * kBlk - band + 1) / kT2 : 0;
+  const int kend = causal ? min(N, qb * kBlk + kBlk) : N;
   const int ntiles = (kend + kT2 - 1) / kT2;
+  const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
   const uint32_t tbytes = (uint32_t)N * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);
   auto issue = [&](KVStage& s, int t) {
@@ -181,21 +189,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int k0 = t * kT2 + sub * kT;
-      if (k0 <= wq_last) {
-        if ((k0 + kT - 1 > qw) || (k0 + kT > N))
-          dq_tile<true>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc);
+      if (k0 <= whi && k0 + kT - 1 >= wlo) {
+        // masked: some pair of the tile is absent for some query of the wave
+        if ((causal && k0 + kT - 1 > qw) || (k0 + kT > N) || (band && k0 < qw + kRowsW - band))
+          dq_tile<true>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale,
+                        qop, oop, nls, ndl, dqacc, causal, band);
         else
-          dq_tile<false>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc);
+          dq_tile<false>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale,
+                         qop, oop, nls, ndl, dqacc, causal, band);
       }
     }
     if (pre) wait_vm_barrier<8>();
     else wait_vm_barrier<0>();
   };
 
-  issue(st0, 0);
-  if (ntiles > 1) issue(st1, 1);
+  issue(st0, t0);
+  if (t0 + 1 < ntiles) issue(st1, t0 + 1);
   wait_vm_barrier<0>();
-  for (int t = 0; t < ntiles; t += 3) {
+  for (int t = t0; t < ntiles; t += 3) {
     step(st0, st2, t);
     if (t + 1 < ntiles) step(st1, st0, t + 1);
     if (t + 2 < ntiles) step(st2, st1, t + 2);
@@ -223,13 +234,16 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
 hipError_t launch_bwd_dq_bf16(const __bf16* q, const __bf16* k, const __bf16* v,
                               const __bf16* dout, const float* nlse, const float* ndelta,
                               __bf16* dq, int64_t heads, int64_t N, double scale,
-                              hipStream_t stream, const Timers& tm) {
+                              const Mask& mk, hipStream_t stream, const Timers& tm) {
   const float c = (float)(scale * 1.4426950408889634);
   const int nb = (int)((N + kBlk - 1) / kBlk);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nb);
   if (hipError_t e = mark(tm.start[kTimerBwdDq], stream)) return e;
-  hipLaunchKernelGGL(bwd_dq_bf16, dim3(grid), dim3(kThreads), 0, stream, q, k, v, dout, nlse,
-                     ndelta, dq, (int)heads, (int)N, nb, c, (float)scale);
+  auto kern = mk.band > 0 ? bwd_dq_bf16<true, true>
+              : mk.causal ? bwd_dq_bf16<true, false>
+                          : bwd_dq_bf16<false, false>;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, dout, nlse, ndelta, dq,
+                     (int)heads, (int)N, nb, c, (float)scale, mk.band);
   if (hipError_t e = mark(tm.stop[kTimerBwdDq], stream)) return e;
   return hipGetLastError();
 }

@@ -52,6 +52,13 @@ constexpr int kBr = kQW * kWaves;       // queries per workgroup
 constexpr int kBc = 64;                 // keys per tile
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 256.0f;          // lazy-max bound on a lane's tile sum (2^8)
+constexpr float kRefInit = -1e30f;      // initial reference exponent (see the kernel)
+
+// A pair (query i, key j) is absent when j >= N, or j > i under the causal
+// predicate, or i - j >= band under a window of band keys.
+__device__ __forceinline__ bool absent(int i, int j, int N, int causal, int band) {
+  return j >= N || (causal && j > i) || (band && i - j >= band);
+}
 
 struct KVStage {
   __bf16 k[kBc * kD];
@@ -95,8 +102,9 @@ __device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][2], float c_
 template <bool MASKED>
 __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __bf16* pscr,
                                          int lane, int k0, int qw, int N, float c_scale,
-                                         const bf16x8_t (&qop)[2][4], floatx16 (&oacc)[2][2],
-                                         float (&mref)[2], float (&lsum)[2]) {
+                                         int causal, int band, const bf16x8_t (&qop)[2][4],
+                                         floatx16 (&oacc)[2][2], float (&mref)[2],
+                                         float (&lsum)[2]) {
   const int i32 = lane & 31, h = lane >> 5;
   // ---- S^T = K Q^T: s[kt][qt] holds keys k0 + 32 kt + acc_row(r, h), query column
   floatx16 s[2][2];
@@ -122,7 +130,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + 32 * kt + acc_row(r, h);
-          s[kt][qt][r] = (j > qi || j >= N) ? -__builtin_inff() : s[kt][qt][r];
+          s[kt][qt][r] = absent(qi, j, N, causal, band) ? -__builtin_inff() : s[kt][qt][r];
         }
       }
   }
@@ -141,7 +149,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(mref[qt], mx * c_scale);
       if (mnew != mref[qt]) {
-        const float alpha = __builtin_amdgcn_exp2f(mref[qt] - mnew);  // 0 when mref = -inf
+        const float alpha = __builtin_amdgcn_exp2f(mref[qt] - mnew);  // 0 from kRefInit
         lsum[qt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
@@ -191,7 +199,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
       for (int jj = 0; jj < kBc; ++jj) {
         const int j = k0 + jj;
         const float pj = (float)pscr[i32 * kBc + jj];
-        if (j > qi || j >= N) continue;
+        if (absent(qi, j, N, causal, band)) continue;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -203,9 +211,14 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
   }
 }
 
+// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does.
+template <bool CAUSAL, bool BANDED>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale) {
+    __bf16* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale,
+    int band_arg) {
+  constexpr int causal = CAUSAL;
+  const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
   __shared__ __bf16 pscr[kWaves][32 * kBc];
   int head, qb;
@@ -215,8 +228,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const size_t base = (size_t)head * N * kD;
   const int qw = qb * kBr + wave * kQW;              // first query of this wave
   const int wq_last = min(qw + kQW, N) - 1;          // last valid query of the wave
-  const int kend = min(N, qb * kBr + kBr);           // keys the workgroup needs
+  // keys the workgroup needs: tiles t0 .. ntiles-1
+  const int t0 = band ? max(0, qb * kBr - band + 1) / kBc : 0;
+  const int kend = causal ? min(N, qb * kBr + kBr) : N;
   const int ntiles = (kend + kBc - 1) / kBc;
+  const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
 
   // Q operand: lane holds q[qw + 32 qt + i32][16 kk + 8 h .. +7]
   bf16x8_t qop[2][4];
@@ -235,7 +251,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b) oacc[a][b] = floatx16{};
-  float mref[2] = {-__builtin_inff(), -__builtin_inff()};
+  // reference exponents start finite, so a tile whose pairs are all absent for
+  // a lane gives it weights exp2(-inf) = 0, and its first present pair takes the
+  // exact path (the weight overflows against kRefInit)
+  float mref[2] = {kRefInit, kRefInit};
   float lsum[2] = {0.f, 0.f};
 
   const uint32_t tbytes = (uint32_t)N * kD * 2;
@@ -248,20 +267,23 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const bool pre = t + 2 < ntiles;
     if (pre) issue(ahead, t + 2);
     const int k0 = t * kBc;
-    if (k0 <= wq_last) {
-      if ((k0 + kBc - 1 > qw) || (k0 + kBc > N))
-        fwd_tile<true>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, qop, oacc, mref, lsum);
+    if (k0 <= whi && k0 + kBc - 1 >= wlo) {
+      // masked: some pair of the tile is absent for some query of the wave
+      if ((causal && k0 + kBc - 1 > qw) || (k0 + kBc > N) || (band && k0 < qw + kQW - band))
+        fwd_tile<true>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band, qop,
+                       oacc, mref, lsum);
       else
-        fwd_tile<false>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, qop, oacc, mref, lsum);
+        fwd_tile<false>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band, qop,
+                        oacc, mref, lsum);
     }
     if (pre) wait_vm_barrier<4>();
     else wait_vm_barrier<0>();
   };
 
-  issue(st0, 0);
-  if (ntiles > 1) issue(st1, 1);
+  issue(st0, t0);
+  if (t0 + 1 < ntiles) issue(st1, t0 + 1);
   wait_vm_barrier<0>();
-  for (int t = 0; t < ntiles; t += 3) {
+  for (int t = t0; t < ntiles; t += 3) {
     step(st0, st2, t);
     if (t + 1 < ntiles) step(st1, st0, t + 1);
     if (t + 2 < ntiles) step(st2, st1, t + 2);
@@ -292,14 +314,17 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 }  // namespace
 
 hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o,
-                           float* lse, int64_t heads, int64_t N, double scale, hipStream_t stream,
-                           const Timers& tm) {
+                           float* lse, int64_t heads, int64_t N, double scale, const Mask& mk,
+                           hipStream_t stream, const Timers& tm) {
   const int nqb = (int)((N + kBr - 1) / kBr);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nqb);
   const float c = (float)(scale * 1.4426950408889634);  // scale * log2(e)
+  auto kern = mk.band > 0 ? attn_fwd_bf16_kernel<true, true>
+              : mk.causal ? attn_fwd_bf16_kernel<true, false>
+                          : attn_fwd_bf16_kernel<false, false>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse,
-                     (int)heads, (int)N, nqb, c);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, (int)heads,
+                     (int)N, nqb, c, mk.band);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }

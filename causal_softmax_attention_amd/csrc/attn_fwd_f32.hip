@@ -37,6 +37,7 @@ constexpr int kBr = kQW * kWaves;       // queries per workgroup
 constexpr int kBc = 64;                 // keys per tile
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kTau = 256.0f;
+constexpr float kRefInit = -1e30f;  // initial reference exponent (see the kernel)
 
 __device__ __forceinline__ floatx16 mma32(float a, float b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -60,11 +61,18 @@ __device__ __forceinline__ bool finite4(float4 x) {
          __builtin_isfinite(x.w);
 }
 
+// A pair (query i, key j) is absent when j >= N, or j > i under the causal
+// predicate, or i - j >= band under a window of band keys.
+__device__ __forceinline__ bool absent(int i, int j, int N, int causal, int band) {
+  return j >= N || (causal && j > i) || (band && i - j >= band);
+}
+
 template <bool MASKED>
 __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, float* pscr,
                                              int lane, int k0, int qw, int N, float c_scale,
-                                             bool vnonfinite, const float (&qreg)[32],
-                                             floatx16 (&oacc)[2], float& mref, float& lsum) {
+                                             int causal, int band, bool vnonfinite,
+                                             const float (&qreg)[32], floatx16 (&oacc)[2],
+                                             float& mref, float& lsum) {
   const int i32 = lane & 31, h = lane >> 5;
   const int qi = qw + i32;
   floatx16 s[2];  // [kt]: scores, then (in place) weights
@@ -88,7 +96,7 @@ __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, f
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + 32 * kt + acc_row(r, h);
-          s[kt][r] = (j > qi || j >= N) ? -__builtin_inff() : s[kt][r];
+          s[kt][r] = absent(qi, j, N, causal, band) ? -__builtin_inff() : s[kt][r];
         }
     }
   };
@@ -118,7 +126,7 @@ __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, f
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(mref, mx * c_scale);
     if (mnew != mref) {
-      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 when mref = -inf
+      const float alpha = __builtin_amdgcn_exp2f(mref - mnew);  // 0 from the initial reference
       lsum *= alpha;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
@@ -153,7 +161,7 @@ __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, f
     for (int jj = 0; jj < kBc; ++jj) {
       const int j = k0 + jj;
       const float pj = pscr[i32 * kBc + jj];
-      if (j > qi || j >= N) continue;
+      if (absent(qi, j, N, causal, band)) continue;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -164,9 +172,14 @@ __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, f
   }
 }
 
+// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does.
+template <bool CAUSAL, bool BANDED>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale) {
+    float* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale,
+    int band_arg) {
+  constexpr int causal = CAUSAL;
+  const int band = BANDED ? band_arg : 0;
   __shared__ Smem sm;
   int head, qb;
   if (!mfma::map_block(blockIdx.x, heads, nqb, true, head, qb)) return;
@@ -175,8 +188,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
   const size_t base = (size_t)head * N * kD;
   const int qw = qb * kBr + wave * kQW;
   const int wq_last = min(qw + kQW, N) - 1;
-  const int kend = min(N, qb * kBr + kBr);
+  // keys of the workgroup's queries: from its first query's window start to
+  // its last query (causal) or the end (full)
+  const int t0 = band ? max(0, qb * kBr - band + 1) / kBc : 0;
+  const int kend = causal ? min(N, qb * kBr + kBr) : N;
   const int ntiles = (kend + kBc - 1) / kBc;
+  const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
   const int qi = qw + i32;
   const bool active = qw < N;  // a wave past the end only joins the barriers
 
@@ -191,7 +208,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
     qreg[4 * c + 3] = x.w;
   }
   floatx16 oacc[2] = {floatx16{}, floatx16{}};  // [dt]: O^T tile, lane holds the query column
-  float mref = -__builtin_inff(), lsum = 0.f;
+  // reference exponent: finite, so a first tile whose pairs are all absent for
+  // this lane gives weights exp2(-inf) = 0 (not -inf - -inf), and the first
+  // tile with a present pair takes the exact path (its weights overflow)
+  float mref = kRefInit, lsum = 0.f;
 
   // staging: a 64-key tile is 1024 16-byte chunks of K and of V, two per
   // thread.  K chunks go row-major (coalesced loads, contiguous stores); V
@@ -224,21 +244,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
     return fin;
   };
 
-  load_tile(0);
+  load_tile(t0);
   // the barrier also ORs "this V tile holds a non-finite value" over the workgroup
   int vnonfinite = __syncthreads_or(!store_tile(0));
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
+  for (int t = t0; t < ntiles; ++t) {
+    const int buf = (t - t0) & 1;
     const bool more = t + 1 < ntiles;
     if (more) load_tile(t + 1);
     const int k0 = t * kBc;
-    if (active && k0 <= wq_last) {
-      if ((k0 + kBc - 1 > qw) || (k0 + kBc > N))
-        fwd_tile_f32<true>(sm.k[buf], sm.vt[buf], sm.p[wave], lane, k0, qw, N, c_scale,
-                           vnonfinite != 0, qreg, oacc, mref, lsum);
+    if (active && k0 <= whi && k0 + kBc - 1 >= wlo) {
+      // masked: some pair of the tile is absent for some query of the wave
+      if ((causal && k0 + kBc - 1 > qw) || (k0 + kBc > N) || (band && k0 < qw + kQW - band))
+        fwd_tile_f32<true>(sm.k[buf], sm.vt[buf], sm.p[wave], lane, k0, qw, N, c_scale, causal,
+                           band, vnonfinite != 0, qreg, oacc, mref, lsum);
       else
-        fwd_tile_f32<false>(sm.k[buf], sm.vt[buf], sm.p[wave], lane, k0, qw, N, c_scale, false,
-                            qreg, oacc, mref, lsum);
+        fwd_tile_f32<false>(sm.k[buf], sm.vt[buf], sm.p[wave], lane, k0, qw, N, c_scale, causal,
+                            band, false, qreg, oacc, mref, lsum);
     }
     const bool fin = more ? store_tile(buf ^ 1) : true;
     vnonfinite = __syncthreads_or(!fin);
@@ -263,14 +284,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
 }  // namespace
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int64_t heads, int64_t N, double scale, hipStream_t stream,
-                          const Timers& tm) {
+                          int64_t heads, int64_t N, double scale, const Mask& mk,
+                          hipStream_t stream, const Timers& tm) {
   const int nqb = (int)((N + kBr - 1) / kBr);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nqb);
   const float c = (float)(scale * 1.4426950408889634);
+  auto kern = mk.band > 0 ? attn_fwd_f32_kernel<true, true>
+              : mk.causal ? attn_fwd_f32_kernel<true, false>
+                          : attn_fwd_f32_kernel<false, false>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
-  hipLaunchKernelGGL(attn_fwd_f32_kernel, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse,
-                     (int)heads, (int)N, nqb, c);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, (int)heads,
+                     (int)N, nqb, c, mk.band);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }

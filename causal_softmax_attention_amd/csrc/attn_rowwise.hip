@@ -8,7 +8,9 @@
 // j <= i is visited by exactly the group that owns it and an absent pair
 // (j > i) is never touched (pages: "Show HN: automatic deduction of
 // FlashAttention kernel from 25 lines of SQL", the join predicate q.t >= k.t and
-// the masks-are-absent-rows check).  The forward keeps a running max and
+// the masks-are-absent-rows check).  The predicate is a parameter: causal
+// (j <= i), every pair, or a causal window (j <= i and i - j < band); each row
+// walks only the stretch of the other side its predicate admits.  The forward keeps a running max and
 // denominator per row (the streaming plan the same page attributes to
 // FlashAttention) and stores lse = m + ln l for the backward.
 #include "common.h"
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v, T* __restrict__ o,
                                                      acc_t<T>* __restrict__ lse, int N, int nqb,
-                                                     acc_t<T> scale) {
+                                                     acc_t<T> scale, int causal, int band) {
   using A = acc_t<T>;
   __shared__ A ks[kTile][kD];
   __shared__ A vs[kTile][kD];
@@ -59,6 +61,7 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
   const int g = threadIdx.x % kG, f0 = kF * g;
   const int i = qb * kRows + threadIdx.x / kG;
   const bool valid = i < N;
+  const int jlo = band ? i - band + 1 : 0, jhi = causal ? i : N - 1;  // this row's keys
 
   A qr[kF], acc[kF];
 #pragma unroll
@@ -67,14 +70,18 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
     acc[f] = 0;
   }
   A m = neg_inf<A>(), l = 0;
-  const int kend = min(N, (qb + 1) * kRows);
-  for (int k0 = 0; k0 < kend; k0 += kTile) {
+  // keys of the block's rows: from its first row's window start to its last row
+  const int kbeg = band ? max(0, qb * kRows - band + 1) / kTile * kTile : 0;
+  const int kend = causal ? min(N, (qb + 1) * kRows) : N;
+  for (int k0 = kbeg; k0 < kend; k0 += kTile) {
     __syncthreads();
     load_tiles(ks, vs, k, v, base, k0, N);
     __syncthreads();
     const int jn = min(kTile, kend - k0);
     for (int jj = 0; jj < jn; ++jj) {
-      if (k0 + jj > i) break;  // pairs j > i do not exist (the whole group leaves together)
+      const int j = k0 + jj;
+      if (j > jhi) break;  // absent pairs past the row (the whole group leaves together)
+      if (j < jlo) continue;
       A s = 0;
 #pragma unroll
       for (int f = 0; f < kF; ++f) s += qr[f] * ks[jj][f0 + f];
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
     const acc_t<T>* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int N, int nkb,
-    acc_t<T> scale) {
+    acc_t<T> scale, int causal, int band) {
   using A = acc_t<T>;
   __shared__ A qs[kTile][kD];
   __shared__ A dos[kTile][kD];
@@ -130,6 +137,7 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
   const int g = threadIdx.x % kG, f0 = kF * g;
   const int j = kb * kRows + threadIdx.x / kG;
   const bool valid = j < N;
+  const int ilo = causal ? j : 0, ihi = band ? j + band - 1 : N - 1;  // this key's queries
   A kr[kF], vr[kF], gk[kF], gv[kF];
 #pragma unroll
   for (int f = 0; f < kF; ++f) {
@@ -138,7 +146,9 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
     gk[f] = 0;
     gv[f] = 0;
   }
-  for (int q0 = kb * kRows; q0 < N; q0 += kTile) {
+  const int qbeg = causal ? kb * kRows : 0;
+  const int qend = band ? min(N, (kb + 1) * kRows + band - 1) : N;
+  for (int q0 = qbeg; q0 < qend; q0 += kTile) {
     __syncthreads();
     load_tiles(qs, dos, q, dout, base, q0, N);
     if (threadIdx.x < kTile) {
@@ -147,9 +157,9 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
       ds_[threadIdx.x] = i < N ? delta[(size_t)head * N + i] : A(0);
     }
     __syncthreads();
-    const int in = min(kTile, N - q0);
+    const int in = min(kTile, qend - q0);
     for (int ii = 0; ii < in; ++ii) {
-      if (q0 + ii < j) continue;  // pair (i, j) exists only for i >= j
+      if (q0 + ii < ilo || q0 + ii > ihi) continue;  // pair (i, j) absent
       A s = 0, dp = 0;
 #pragma unroll
       for (int f = 0; f < kF; ++f) {
@@ -181,7 +191,8 @@ template <typename T>
 __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
-    const acc_t<T>* __restrict__ delta, T* __restrict__ dq, int N, int nqb, acc_t<T> scale) {
+    const acc_t<T>* __restrict__ delta, T* __restrict__ dq, int N, int nqb, acc_t<T> scale,
+    int causal, int band) {
   using A = acc_t<T>;
   __shared__ A ks[kTile][kD];
   __shared__ A vs[kTile][kD];
@@ -200,14 +211,18 @@ __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
   }
   const A li = valid ? lse[(size_t)head * N + i] : A(0);
   const A di = valid ? delta[(size_t)head * N + i] : A(0);
-  const int kend = min(N, (qb + 1) * kRows);
-  for (int k0 = 0; k0 < kend; k0 += kTile) {
+  const int jlo = band ? i - band + 1 : 0, jhi = causal ? i : N - 1;
+  const int kbeg = band ? max(0, qb * kRows - band + 1) / kTile * kTile : 0;
+  const int kend = causal ? min(N, (qb + 1) * kRows) : N;
+  for (int k0 = kbeg; k0 < kend; k0 += kTile) {
     __syncthreads();
     load_tiles(ks, vs, k, v, base, k0, N);
     __syncthreads();
     const int jn = min(kTile, kend - k0);
     for (int jj = 0; jj < jn; ++jj) {
-      if (k0 + jj > i) break;
+      const int j = k0 + jj;
+      if (j > jhi) break;
+      if (j < jlo) continue;
       A s = 0, dp = 0;
 #pragma unroll
       for (int f = 0; f < kF; ++f) {
@@ -232,12 +247,13 @@ __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
 
 template <typename T>
 hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64_t heads,
-                      int64_t N, double scale, hipStream_t stream, const Timers& tm) {
+                      int64_t N, double scale, const Mask& mk, hipStream_t stream,
+                      const Timers& tm) {
   using A = acc_t<T>;
   const int nqb = (int)((N + kRows - 1) / kRows);
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
   hipLaunchKernelGGL(fwd_rowwise<T>, dim3((unsigned)(heads * nqb)), dim3(kThr), 0, stream, q, k,
-                     v, o, (A*)lse, (int)N, nqb, (A)scale);
+                     v, o, (A*)lse, (int)N, nqb, (A)scale, mk.causal, mk.band);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }
@@ -250,7 +266,8 @@ size_t bwd_workspace_bytes(int64_t heads, int64_t N) {
 template <typename T>
 hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* dout,
                       const void* lse, T* dq, T* dk, T* dv, void* workspace, int64_t heads,
-                      int64_t N, double scale, hipStream_t stream, const Timers& tm) {
+                      int64_t N, double scale, const Mask& mk, hipStream_t stream,
+                      const Timers& tm) {
   using A = acc_t<T>;
   A* delta = (A*)workspace;
   const int64_t rows = heads * N;
@@ -261,22 +278,23 @@ hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* d
   const int nb = (int)((N + kRows - 1) / kRows);
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
   hipLaunchKernelGGL(bwd_dkdv_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q,
-                     k, v, dout, (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale);
+                     k, v, dout, (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale, mk.causal,
+                     mk.band);
   if (hipError_t e = mark(tm.stop[kTimerBwdDkdv], stream)) return e;
   if (hipError_t e = mark(tm.start[kTimerBwdDq], stream)) return e;
   hipLaunchKernelGGL(bwd_dq_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q, k,
-                     v, dout, (const A*)lse, delta, dq, (int)N, nb, (A)scale);
+                     v, dout, (const A*)lse, delta, dq, (int)N, nb, (A)scale, mk.causal, mk.band);
   if (hipError_t e = mark(tm.stop[kTimerBwdDq], stream)) return e;
   return hipGetLastError();
 }
 
 #define ATTN_INSTANTIATE(T)                                                                     \
   template hipError_t launch_fwd<T>(const T*, const T*, const T*, T*, void*, int64_t, int64_t, \
-                                    double, hipStream_t, const Timers&);                        \
+                                    double, const Mask&, hipStream_t, const Timers&);           \
   template size_t bwd_workspace_bytes<T>(int64_t, int64_t);                                    \
   template hipError_t launch_bwd<T>(const T*, const T*, const T*, const T*, const T*,          \
                                     const void*, T*, T*, T*, void*, int64_t, int64_t, double,  \
-                                    hipStream_t, const Timers&);
+                                    const Mask&, hipStream_t, const Timers&);
 ATTN_INSTANTIATE(double)
 ATTN_INSTANTIATE(float)  // the float32 backward (its forward runs on MFMA, attn_fwd_f32.hip)
 

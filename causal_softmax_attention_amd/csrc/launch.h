@@ -18,12 +18,23 @@ enum { kTimerFwd = 0, kTimerBwdPre = 1, kTimerBwdDkdv = 2, kTimerBwdDq = 3, kTim
 
 inline hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
 
+// Which (query i, key j) pairs exist (the join predicate): j < N and
+//   causal != 0: j <= i;   band > 0: i - j < band   (band 0: no lower limit).
+// causal = 1, band = 0 is the causal view; causal = 0, band = 0 every pair;
+// causal = 1, band = w a causal window of w keys.  (causal = 0 with band > 0
+// is not used.)
+struct Mask {
+  int causal = 1;
+  int band = 0;
+};
+
 // Row-per-group kernels (attn_rowwise.hip): forward and backward of `heads`
 // independent heads of N tokens, D = 64.  T is double or float; lse is double
 // for double, float otherwise.
 template <typename T>
 hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64_t heads,
-                      int64_t N, double scale, hipStream_t stream, const Timers& tm);
+                      int64_t N, double scale, const Mask& mk, hipStream_t stream,
+                      const Timers& tm);
 
 // Backward workspace bytes and launch (dq, dk, dv from q, k, v, o, dout, lse).
 template <typename T>
@@ -32,17 +43,18 @@ size_t bwd_workspace_bytes(int64_t heads, int64_t N);
 template <typename T>
 hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* dout,
                       const void* lse, T* dq, T* dk, T* dv, void* workspace, int64_t heads,
-                      int64_t N, double scale, hipStream_t stream, const Timers& tm);
+                      int64_t N, double scale, const Mask& mk, hipStream_t stream,
+                      const Timers& tm);
 
 // float32 forward on MFMA tiles (attn_fwd_f32.hip).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int64_t heads, int64_t N, double scale, hipStream_t stream,
-                          const Timers& tm);
+                          int64_t heads, int64_t N, double scale, const Mask& mk,
+                          hipStream_t stream, const Timers& tm);
 
 // bfloat16 forward on MFMA tiles (attn_fwd_bf16.hip).
 hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o,
-                           float* lse, int64_t heads, int64_t N, double scale, hipStream_t stream,
-                           const Timers& tm);
+                           float* lse, int64_t heads, int64_t N, double scale, const Mask& mk,
+                           hipStream_t stream, const Timers& tm);
 
 // bfloat16 backward on MFMA tiles (attn_bwd_bf16.hip); the workspace holds two floats
 // per row (-delta and -lse / scale).
@@ -50,13 +62,13 @@ size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N);
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
                            const __bf16* dout, const float* lse, __bf16* dq, __bf16* dk,
                            __bf16* dv, void* workspace, int64_t heads, int64_t N, double scale,
-                           hipStream_t stream, const Timers& tm);
+                           const Mask& mk, hipStream_t stream, const Timers& tm);
 
 // The dQ pass alone (attn_bwd_dq_bf16.hip), from the prep kernel's per-row values.
 hipError_t launch_bwd_dq_bf16(const __bf16* q, const __bf16* k, const __bf16* v,
                               const __bf16* dout, const float* nlse, const float* ndelta,
                               __bf16* dq, int64_t heads, int64_t N, double scale,
-                              hipStream_t stream, const Timers& tm);
+                              const Mask& mk, hipStream_t stream, const Timers& tm);
 
 hipError_t launch_nw(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,
                      const float* sx, const float* sy, const float* sv, float denom, float* out,

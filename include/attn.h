@@ -28,7 +28,7 @@
  *     ATTN_EUNSUPPORTED.  attn_last_error() returns the calling thread's last
  *     message.  The library keeps no other state; calls from several host
  *     threads are safe.
- *   - Outputs must not alias inputs, except dout == o in attn_causal_bwd.
+ *   - Outputs must not alias inputs, except dout == o in the backward passes.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -59,6 +59,17 @@ enum {
   ATTN_EHIP = 3          /* the HIP runtime rejected a launch */
 };
 
+/* Join predicate: which (query i, key j) pairs exist (pages: "Show HN:
+ * automatic deduction of FlashAttention kernel from 25 lines of SQL", the view
+ * `attention` joins q and k on q.t >= k.t, and the same post's claim that the
+ * fused plan follows for any softmax-weighted join).  An absent pair takes no
+ * part in the max, the sum or the weighted average.
+ *   ATTN_MASK_CAUSAL  j <= i                          (the view `attention`)
+ *   ATTN_MASK_FULL    every j                          (the join with no predicate)
+ *   ATTN_MASK_WINDOW  j <= i and i - j < window        (a causal band of `window`
+ *                     keys; window >= 1, and a window >= N is the causal mask) */
+typedef enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_FULL = 1, ATTN_MASK_WINDOW = 2 } attn_mask_t;
+
 /* Forward pass (the view `attention`: scores from the join q.t >= k.t, the
  * row max subtracted, normalised by the row sum, weighted sum of v).
  *   dtype  attn_dtype_t of q, k, v, o
@@ -69,6 +80,17 @@ enum {
 ATTN_API int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
                     const void* q, const void* k, const void* v, void* o, void* lse,
                     void* stream);
+
+/* The forward pass under any join predicate of attn_mask_t: as
+ * attn_causal_fwd, with
+ *   mask    ATTN_MASK_CAUSAL, ATTN_MASK_FULL or ATTN_MASK_WINDOW
+ *   window  keys per query for ATTN_MASK_WINDOW (>= 1); ignored otherwise
+ * attn_causal_fwd(...) is attn_fwd(..., ATTN_MASK_CAUSAL, 0, ...).
+ * Returns ATTN_OK / ATTN_EINVAL (also for an unknown mask or window < 1) /
+ * ATTN_EUNSUPPORTED / ATTN_EHIP. */
+ATTN_API int attn_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                      int mask, int64_t window, const void* q, const void* k, const void* v,
+                      void* o, void* lse, void* stream);
 
 /* Bytes of device workspace attn_causal_bwd needs for these sizes (0 on an
  * invalid request).  The caller allocates it; its contents need not be
@@ -88,6 +110,20 @@ ATTN_API int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t
                     const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const void* lse, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for attn_bwd (the same for every mask; equal to
+ * attn_causal_bwd_workspace_bytes). */
+ATTN_API size_t attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D);
+
+/* The backward pass under any join predicate: as attn_causal_bwd, with mask
+ * and window as in attn_fwd; lse must come from attn_fwd with the same mask
+ * and window.  attn_causal_bwd(...) is attn_bwd(..., ATTN_MASK_CAUSAL, 0, ...).
+ * Returns ATTN_OK / ATTN_EINVAL (also for an unknown mask or window < 1) /
+ * ATTN_EUNSUPPORTED / ATTN_EHIP. */
+ATTN_API int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                      int mask, int64_t window, const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const void* lse, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Nadaraya-Watson control (the pages' NADARAYA_WATSON query): for every target
  * p, out_p = sum_q w_pq v_q / sum_q w_pq over ALL sources q (a cross join),

@@ -51,24 +51,30 @@ class Guarded:
                     torch.equal(self.raw[p + n:], self.ref[p + n:]))
 
 
-def run_fwd(q, k, v, scale=0.125, guard=True):
+def run_fwd(q, k, v, scale=0.125, guard=True, mask=None, window=0):
+    """The forward through attn_causal_fwd, or attn_fwd when a mask is named."""
     B, H, N, D = q.shape
+    call = (lambda **kw: csa.attn_causal_fwd(q, k, v, scale, **kw)) if mask is None else \
+        (lambda **kw: csa.attn_fwd(q, k, v, scale, mask, window, **kw))
     if not guard:
-        return csa.attn_causal_fwd(q, k, v, scale)
+        return call()
     lse_dt = torch.float64 if q.dtype == torch.float64 else torch.float32
     og, lg = Guarded((B, H, N, D), q.dtype), Guarded((B, H, N), lse_dt)
-    o, lse = csa.attn_causal_fwd(q, k, v, scale, o=og.view, lse=lg.view)
+    o, lse = call(o=og.view, lse=lg.view)
     torch.cuda.synchronize()
     assert og.intact() and lg.intact(), "forward wrote outside its outputs"
     return o, lse
 
 
-def run_bwd(q, k, v, o, dout, lse, scale=0.125, guard=True):
+def run_bwd(q, k, v, o, dout, lse, scale=0.125, guard=True, mask=None, window=0):
+    """The backward through attn_causal_bwd, or attn_bwd when a mask is named."""
+    call = (lambda **kw: csa.attn_causal_bwd(q, k, v, o, dout, lse, scale, **kw)) \
+        if mask is None else \
+        (lambda **kw: csa.attn_bwd(q, k, v, o, dout, lse, scale, mask, window, **kw))
     if not guard:
-        return csa.attn_causal_bwd(q, k, v, o, dout, lse, scale)
+        return call()
     gs = [Guarded(tuple(q.shape), q.dtype) for _ in range(3)]
-    dq, dk, dv = csa.attn_causal_bwd(q, k, v, o, dout, lse, scale, dq=gs[0].view,
-                                     dk=gs[1].view, dv=gs[2].view)
+    dq, dk, dv = call(dq=gs[0].view, dk=gs[1].view, dv=gs[2].view)
     torch.cuda.synchronize()
     assert all(g.intact() for g in gs), "backward wrote outside its outputs"
     return dq, dk, dv

@@ -29,8 +29,10 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["attn_causal_fwd", "attn_causal_bwd",
-                                         "attn_causal_bwd_workspace_bytes", "nw_gauss_average",
-                                         "attn_set_kernel_timer", "attn_last_error"])
+                                         "attn_causal_bwd_workspace_bytes", "attn_fwd",
+                                         "attn_bwd", "attn_bwd_workspace_bytes",
+                                         "nw_gauss_average", "attn_set_kernel_timer",
+                                         "attn_last_error"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -46,7 +48,8 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_header_compiles_as_c(tmp_path):
     src = tmp_path / "t.c"
-    src.write_text('#include "attn.h"\nint main(void){return ATTN_OK + ATTN_BF16;}\n')
+    src.write_text('#include "attn.h"\n'
+                   'int main(void){return ATTN_OK + ATTN_BF16 + ATTN_MASK_WINDOW;}\n')
     subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-c",
                     str(src), "-o", str(tmp_path / "t.o")], check=True)
 
@@ -117,6 +120,41 @@ def bwd(L, ws_bytes=None, **over):
 def test_bwd_rejects(L, kw, code):
     assert bwd(L, **kw) == code
     assert csa.attn_last_error() != ""
+
+
+def mfwd(L, mask, window, **kw):
+    a = dict(dtype=2, B=1, H=1, N=16, D=64, scale=0.125)
+    a.update(kw)
+    return L.attn_fwd(a["dtype"], a["B"], a["H"], a["N"], a["D"], a["scale"], mask, window, P,
+                      P, P, ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), None)
+
+
+def mbwd(L, mask, window, **kw):
+    a = dict(dtype=2, B=1, H=1, N=16, D=64, scale=0.125)
+    a.update(kw)
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+    need = L.attn_bwd_workspace_bytes(2, 1, 1, 16, 64)
+    return L.attn_bwd(a["dtype"], a["B"], a["H"], a["N"], a["D"], a["scale"], mask, window,
+                      *p, need, None)
+
+
+@pytest.mark.parametrize("mask,window", [(3, 0), (-1, 0), (csa.ATTN_MASK_WINDOW, 0),
+                                         (csa.ATTN_MASK_WINDOW, -5)])
+def test_mask_rejects(L, mask, window):
+    """An unknown mask kind, or a window narrower than one key, is refused before
+    any launch, by both passes."""
+    assert mfwd(L, mask, window) == csa.ATTN_EINVAL
+    assert "mask" in csa.attn_last_error() or "window" in csa.attn_last_error()
+    assert mbwd(L, mask, window) == csa.ATTN_EINVAL
+
+
+def test_masked_entry_points_check_sizes_first(L):
+    for m in (csa.ATTN_MASK_CAUSAL, csa.ATTN_MASK_FULL, csa.ATTN_MASK_WINDOW):
+        assert mfwd(L, m, 4, D=32) == csa.ATTN_EUNSUPPORTED
+        assert mfwd(L, m, 4, N=0) == csa.ATTN_EINVAL
+        assert mbwd(L, m, 4, scale=0.0) == csa.ATTN_EINVAL
+    assert L.attn_bwd_workspace_bytes(2, 2, 3, 100, 64) == \
+        L.attn_causal_bwd_workspace_bytes(2, 2, 3, 100, 64)
 
 
 def test_nw_rejects(L):
