@@ -95,10 +95,11 @@ def make_inputs(name):
 
 
 def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask="causal",
-                   window=0):
+                   window=0, fused=False):
     """Run `steps` timed steps; returns (ms_per_step, {slot: mean ms}, outputs).
     The causal predicate goes through attn_causal_fwd / _bwd, others through
-    attn_fwd / attn_bwd."""
+    attn_fwd / attn_bwd; fused: attn_fwd_train (forward + loss + the
+    backward's per-row values) and attn_bwd_from_fwd."""
     import torch
 
     import causal_softmax_attention_amd as csa
@@ -112,8 +113,13 @@ def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask=
     ws = torch.empty(max(16, csa.attn_causal_bwd_workspace_bytes(code, B, H, N, D)),
                      dtype=torch.uint8, device=q.device)
 
+    loss = torch.empty(1, dtype=torch.float64, device=q.device)
+
     def step():
-        if mask == "causal":
+        if fused:
+            csa.attn_fwd_train(q, k, v, 0.125, mask, window, o=o, lse=lse, workspace=ws, loss=loss)
+            csa.attn_bwd_from_fwd(q, k, v, o, lse, ws, 0.125, mask, window, dq=dq, dk=dk, dv=dv)
+        elif mask == "causal":
             csa.attn_causal_fwd(q, k, v, 0.125, o=o, lse=lse)
             if with_bwd:
                 csa.attn_causal_bwd(q, k, v, o, o, lse, 0.125, dq=dq, dk=dk, dv=dv, workspace=ws)
@@ -126,7 +132,8 @@ def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask=
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    slots = [csa.TIMER_FWD] + ([csa.TIMER_BWD_PRE, csa.TIMER_BWD_DKDV, csa.TIMER_BWD_DQ]
+    slots = [csa.TIMER_FWD] + ([csa.TIMER_BWD_DKDV, csa.TIMER_BWD_DQ] if fused else
+                               [csa.TIMER_BWD_PRE, csa.TIMER_BWD_DKDV, csa.TIMER_BWD_DQ]
                                if with_bwd else [])
     events = []
     if per_kernel:
@@ -206,6 +213,15 @@ def secondary(steps):
     out["bf16_32k_fwd_bwd"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
                                "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
                                "kernels_ms": per}
+    del q, k, v
+    # the same step with the loss fused into the forward (attn_fwd_train +
+    # attn_bwd_from_fwd): the backward's per-row pass is folded away
+    a, (q, k, v), _ = make_inputs("bf16_4k")
+    ms, _, per, _ = time_attention(q, k, v, steps, 2, fused=True)
+    fl = 14 * D * pairs(256, 4096)
+    out["bf16_4k_train_step_fused_loss"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
+                                            "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
+                                            "kernels_ms": per}
     del q, k, v
     # the other join predicates on the same 8 x 32 x 4096 bf16 inputs; flops
     # count each predicate's own pairs (N^2 per head for the full one)

@@ -53,6 +53,13 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
                                i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_bwd.restype = ctypes.c_int
+        L.attn_fwd_train.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
+                                     ctypes.c_int, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+        L.attn_fwd_train.restype = ctypes.c_int
+        L.attn_bwd_from_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
+                                        ctypes.c_int, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                        sz, vp]
+        L.attn_bwd_from_fwd.restype = ctypes.c_int
         L.nw_gauss_average.argtypes = [i64, vp, vp, i64, vp, vp, vp, ctypes.c_float, vp, vp]
         L.nw_gauss_average.restype = ctypes.c_int
         L.attn_set_kernel_timer.argtypes = [ctypes.c_int, vp, vp]
@@ -179,6 +186,38 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, mask: str = "c
     return dq, dk, dv
 
 
+def attn_fwd_train(q, k, v, scale: float = DEFAULT_SCALE, mask: str = "causal", window: int = 0,
+                   o=None, lse=None, workspace=None, loss=None, stream=None):
+    """Forward of the training step with the loss sum(o^2)/2 fused in; returns
+    (o, lse, loss, workspace): loss is a one-element float64 device tensor, and
+    the workspace carries the per-row values attn_bwd_from_fwd reads."""
+    import torch
+    (B, H, N, D), o, lse = _fwd_args(q, k, v, o, lse)
+    code = _dtype_code(q)
+    if workspace is None:
+        workspace = torch.empty(max(attn_bwd_workspace_bytes(code, B, H, N, D), 16),
+                                dtype=torch.uint8, device=q.device)
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float64, device=q.device)
+    _check(lib().attn_fwd_train(code, B, H, N, D, float(scale), _mask_code(mask), int(window),
+                                _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _ptr(loss),
+                                _stream(q, stream)))
+    return o, lse, loss, workspace
+
+
+def attn_bwd_from_fwd(q, k, v, o, lse, workspace, scale: float = DEFAULT_SCALE,
+                      mask: str = "causal", window: int = 0, dq=None, dk=None, dv=None,
+                      stream=None):
+    """Gradients (dq, dk, dv) of the loss sum(o^2)/2 from attn_fwd_train's outputs."""
+    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, o, dq, dk, dv, workspace)
+    _check(lib().attn_bwd_from_fwd(code, B, H, N, D, float(scale), _mask_code(mask), int(window),
+                                   _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dq),
+                                   _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(q, stream)))
+    return dq, dk, dv
+
+
 def nw_gauss_average(tx, ty, sx, sy, sv, denom: float = 0.25, out=None, stream=None):
     """Nadaraya-Watson average at every target; float32 1-D device tensors."""
     import torch
@@ -208,6 +247,6 @@ def attn_set_kernel_timer(slot: int, start, stop):
 
 
 __all__ = ["attn_causal_fwd", "attn_causal_bwd", "attn_causal_bwd_workspace_bytes", "attn_fwd",
-           "attn_bwd", "attn_bwd_workspace_bytes", "MASKS",
+           "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_train", "attn_bwd_from_fwd", "MASKS",
            "nw_gauss_average", "attn_set_kernel_timer", "attn_last_error", "lib", "AttnError",
            "ATTN_F64", "ATTN_F32", "ATTN_BF16"]

@@ -73,13 +73,27 @@ int make_mask(int mask, int64_t window, int64_t N, attn::Mask& mk) {
   }
 }
 
-}  // namespace
+// Workspace of the backward: its per-row values, then (from a 256-byte
+// boundary) kLossParts doubles that the loss sum of attn_fwd_train uses.
+size_t rows_bytes(int dtype, int64_t heads, int64_t N) {
+  switch (dtype) {
+    case ATTN_F64: return attn::bwd_workspace_bytes<double>(heads, N);
+    case ATTN_F32: return attn::bwd_workspace_bytes<float>(heads, N);
+    default: return attn::bwd_workspace_bytes_bf16(heads, N);
+  }
+}
+size_t parts_offset(int dtype, int64_t heads, int64_t N) {
+  return (rows_bytes(dtype, heads, N) + 255) / 256 * 256;
+}
+size_t workspace_bytes_for(int dtype, int64_t heads, int64_t N) {
+  return parts_offset(dtype, heads, N) + attn::kLossParts * sizeof(double);
+}
 
-extern "C" {
-
-int attn_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+// attn_fwd, and with bwd_ws non-null the forward of attn_fwd_train (which
+// checks the workspace itself).
+int fwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
              int64_t window, const void* q, const void* k, const void* v, void* o, void* lse,
-             void* stream) {
+             void* bwd_ws, hipStream_t s) {
   if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
   attn::Mask mk;
   if (int rc = make_mask(mask, window, N, mk)) return rc;
@@ -94,48 +108,36 @@ int attn_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
     if (overlap(o, tb, p, tb) || overlap(lse, lb, p, tb))
       return fail(ATTN_EINVAL, "outputs must not alias inputs");
   if (overlap(o, tb, lse, lb)) return fail(ATTN_EINVAL, "o and lse overlap");
-  hipStream_t s = (hipStream_t)stream;
+  if (bwd_ws) {
+    const size_t wb = workspace_bytes_for(dtype, heads, N);
+    const void* all[] = {q, k, v, o};
+    for (const void* p : all)
+      if (overlap(bwd_ws, wb, p, tb)) return fail(ATTN_EINVAL, "workspace aliases a tensor");
+    if (overlap(bwd_ws, wb, lse, lb)) return fail(ATTN_EINVAL, "workspace aliases lse");
+  }
   hipError_t e;
   switch (dtype) {
     case ATTN_F64:
       e = attn::launch_fwd<double>((const double*)q, (const double*)k, (const double*)v,
-                                   (double*)o, lse, heads, N, scale, mk, s, g_tm);
+                                   (double*)o, lse, heads, N, scale, mk, bwd_ws, s, g_tm);
       break;
     case ATTN_F32:
       e = attn::launch_fwd_f32((const float*)q, (const float*)k, (const float*)v, (float*)o,
-                               (float*)lse, heads, N, scale, mk, s, g_tm);
+                               (float*)lse, heads, N, scale, mk, bwd_ws, s, g_tm);
       break;
     default:
       e = attn::launch_fwd_bf16((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                                (__bf16*)o, (float*)lse, heads, N, scale, mk, s, g_tm);
+                                (__bf16*)o, (float*)lse, heads, N, scale, mk, bwd_ws, s, g_tm);
   }
-  return hip_status(e, "attn_fwd launch");
+  return hip_status(e, "forward launch");
 }
 
-int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                    const void* q, const void* k, const void* v, void* o, void* lse,
-                    void* stream) {
-  return attn_fwd(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, q, k, v, o, lse, stream);
-}
-
-size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
-  if (check_sizes(dtype, B, H, N, D, 1.0) != ATTN_OK) return 0;
-  const int64_t heads = B * H;
-  switch (dtype) {
-    case ATTN_F64: return attn::bwd_workspace_bytes<double>(heads, N);
-    case ATTN_F32: return attn::bwd_workspace_bytes<float>(heads, N);
-    default: return attn::bwd_workspace_bytes_bf16(heads, N);
-  }
-}
-
-size_t attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
-  return attn_causal_bwd_workspace_bytes(dtype, B, H, N, D);
-}
-
-int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+// attn_bwd; prepared: the workspace already holds the per-row values the
+// forward of attn_fwd_train wrote (dout is o).
+int bwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
              int64_t window, const void* q, const void* k, const void* v, const void* o,
              const void* dout, const void* lse, void* dq, void* dk, void* dv, void* workspace,
-             size_t workspace_bytes, void* stream) {
+             size_t workspace_bytes, bool prepared, hipStream_t s) {
   if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
   attn::Mask mk;
   if (int rc = make_mask(mask, window, N, mk)) return rc;
@@ -144,11 +146,11 @@ int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
   const void* all[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
   for (const void* p : all)
     if (!aligned16(p)) return fail(ATTN_EINVAL, "pointers must be 16-byte aligned");
-  const size_t need = attn_causal_bwd_workspace_bytes(dtype, B, H, N, D);
+  const int64_t heads = B * H;
+  const size_t need = workspace_bytes_for(dtype, heads, N);
   if (workspace_bytes < need)
     return fail(ATTN_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
                 workspace_bytes, need);
-  const int64_t heads = B * H;
   const size_t tb = (size_t)heads * N * D * elem_size(dtype);
   const size_t lb = (size_t)heads * N * (dtype == ATTN_F64 ? 8 : 4);
   const void* ins[] = {q, k, v, o, dout};
@@ -164,28 +166,61 @@ int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
   for (const void* r : ins)
     if (overlap(workspace, need, r, tb)) return fail(ATTN_EINVAL, "workspace aliases an input");
   if (overlap(workspace, need, lse, lb)) return fail(ATTN_EINVAL, "workspace aliases lse");
-  hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   switch (dtype) {
     case ATTN_F64:
       e = attn::launch_bwd<double>((const double*)q, (const double*)k, (const double*)v,
                                    (const double*)o, (const double*)dout, lse, (double*)dq,
-                                   (double*)dk, (double*)dv, workspace, heads, N, scale, mk, s,
-                                   g_tm);
+                                   (double*)dk, (double*)dv, workspace, heads, N, scale, mk,
+                                   prepared, s, g_tm);
       break;
     case ATTN_F32:
       e = attn::launch_bwd<float>((const float*)q, (const float*)k, (const float*)v,
                                   (const float*)o, (const float*)dout, lse, (float*)dq,
-                                  (float*)dk, (float*)dv, workspace, heads, N, scale, mk, s,
-                                  g_tm);
+                                  (float*)dk, (float*)dv, workspace, heads, N, scale, mk,
+                                  prepared, s, g_tm);
       break;
     default:
       e = attn::launch_bwd_bf16((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                                 (const __bf16*)o, (const __bf16*)dout, (const float*)lse,
                                 (__bf16*)dq, (__bf16*)dk, (__bf16*)dv, workspace, heads, N, scale,
-                                mk, s, g_tm);
+                                mk, prepared, s, g_tm);
   }
-  return hip_status(e, "attn_bwd launch");
+  return hip_status(e, "backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+             int64_t window, const void* q, const void* k, const void* v, void* o, void* lse,
+             void* stream) {
+  return fwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, lse, nullptr,
+                  (hipStream_t)stream);
+}
+
+int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                    const void* q, const void* k, const void* v, void* o, void* lse,
+                    void* stream) {
+  return attn_fwd(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, q, k, v, o, lse, stream);
+}
+
+size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
+  if (check_sizes(dtype, B, H, N, D, 1.0) != ATTN_OK) return 0;
+  return workspace_bytes_for(dtype, B * H, N);
+}
+
+size_t attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
+  return attn_causal_bwd_workspace_bytes(dtype, B, H, N, D);
+}
+
+int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+             int64_t window, const void* q, const void* k, const void* v, const void* o,
+             const void* dout, const void* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  return bwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, dout, lse, dq, dk, dv,
+                  workspace, workspace_bytes, false, (hipStream_t)stream);
 }
 
 int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
@@ -194,6 +229,43 @@ int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, doubl
                     void* workspace, size_t workspace_bytes, void* stream) {
   return attn_bwd(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, q, k, v, o, dout, lse, dq, dk,
                   dv, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_train(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+                   int64_t window, const void* q, const void* k, const void* v, void* o,
+                   void* lse, void* workspace, size_t workspace_bytes, double* loss,
+                   void* stream) {
+  if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
+  if (!workspace || !loss) return fail(ATTN_EINVAL, "null pointer argument");
+  if (!aligned16(workspace) || ((uintptr_t)loss & 7u))
+    return fail(ATTN_EINVAL, "workspace must be 16-byte and loss 8-byte aligned");
+  const int64_t heads = B * H;
+  const size_t need = workspace_bytes_for(dtype, heads, N);
+  if (workspace_bytes < need)
+    return fail(ATTN_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
+                workspace_bytes, need);
+  const size_t tb = (size_t)heads * N * D * elem_size(dtype);
+  const size_t lb = (size_t)heads * N * (dtype == ATTN_F64 ? 8 : 4);
+  const void* all[] = {q, k, v, o};
+  for (const void* p : all)
+    if (overlap(loss, 8, p, tb)) return fail(ATTN_EINVAL, "loss aliases a tensor");
+  if (overlap(loss, 8, lse, lb) || overlap(loss, 8, workspace, need))
+    return fail(ATTN_EINVAL, "loss aliases lse or the workspace");
+  hipStream_t s = (hipStream_t)stream;
+  if (int rc = fwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, lse, workspace, s))
+    return rc;
+  const int kind = dtype == ATTN_F64 ? 0 : dtype == ATTN_F32 ? 1 : 2;
+  double* parts = (double*)((char*)workspace + parts_offset(dtype, heads, N));
+  return hip_status(attn::launch_loss(kind, workspace, heads * N, parts, loss, s),
+                    "attn_fwd_train loss launch");
+}
+
+int attn_bwd_from_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                      int mask, int64_t window, const void* q, const void* k, const void* v,
+                      const void* o, const void* lse, void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, o, lse, dq, dk, dv,
+                  workspace, workspace_bytes, true, (hipStream_t)stream);
 }
 
 int nw_gauss_average(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,

@@ -347,17 +347,19 @@ size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N) {
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
                            const __bf16* dout, const float* lse, __bf16* dq, __bf16* dk,
                            __bf16* dv, void* workspace, int64_t heads, int64_t N, double scale,
-                           const Mask& mk, hipStream_t stream, const Timers& tm) {
+                           const Mask& mk, bool prepared, hipStream_t stream, const Timers& tm) {
   const int64_t rows = heads * N;
   float* ndelta = (float*)workspace;
   float* nlse = ndelta + rows;
   const float c = (float)(scale * 1.4426950408889634);
   const int nb = (int)((N + kBlk - 1) / kBlk);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nb);
-  if (hipError_t e = mark(tm.start[kTimerBwdPre], stream)) return e;
-  hipLaunchKernelGGL(bwd_prep_bf16, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, o,
-                     dout, lse, ndelta, nlse, (float)(1.0 / scale), rows);
-  if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
+  if (!prepared) {  // else the forward already wrote both per-row values (dO = O)
+    if (hipError_t e = mark(tm.start[kTimerBwdPre], stream)) return e;
+    hipLaunchKernelGGL(bwd_prep_bf16, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, o,
+                       dout, lse, ndelta, nlse, (float)(1.0 / scale), rows);
+    if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
+  }
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
   auto kern = mk.band > 0 ? bwd_dkdv_bf16<true> : bwd_dkdv_bf16<false>;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, dout, nlse, ndelta, dk,

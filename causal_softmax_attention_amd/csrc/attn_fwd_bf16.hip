@@ -216,7 +216,7 @@ template <bool CAUSAL, bool BANDED>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale,
-    int band_arg) {
+    int band_arg, float* __restrict__ ndelta, float* __restrict__ nlse, float inv_scale) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
@@ -289,13 +289,16 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
     if (t + 2 < ntiles) step(st2, st1, t + 2);
   }
 
-  // ---- epilogue: l over both lane halves, O = O^T / l, lse = (m + log2 l) ln 2
+  // ---- epilogue: l over both lane halves, O = O^T / l, lse = (m + log2 l) ln 2.
+  // With ndelta given (the loss sum(o^2)/2, so dO = O), also the backward's
+  // per-row values from the stored bf16 row: -delta_i = -|o_i|^2 and -lse_i / scale.
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     const int qi = qw + 32 * qt + i32;
     const float l = lsum[qt] + __shfl_xor(lsum[qt], 32);
     const float inv = 1.0f / l;
     if (qi < N) {
+      float sq = 0.f;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -305,8 +308,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
           w.x = pack_bf16(oacc[dt][qt][4 * g + 0] * inv, oacc[dt][qt][4 * g + 1] * inv);
           w.y = pack_bf16(oacc[dt][qt][4 * g + 2] * inv, oacc[dt][qt][4 * g + 3] * inv);
           *(uint2*)(o + base + (size_t)qi * kD + d) = w;
+          if (ndelta) {
+            const float x0 = __uint_as_float(w.x << 16), x1 = __uint_as_float(w.x & 0xffff0000u);
+            const float x2 = __uint_as_float(w.y << 16), x3 = __uint_as_float(w.y & 0xffff0000u);
+            sq = fmaf(x0, x0, fmaf(x1, x1, fmaf(x2, x2, fmaf(x3, x3, sq))));
+          }
         }
-      if (h == 0) lse[(size_t)head * N + qi] = (mref[qt] + __log2f(l)) * kLn2;
+      const float lse_i = (mref[qt] + __log2f(l)) * kLn2;
+      if (h == 0) lse[(size_t)head * N + qi] = lse_i;
+      if (ndelta) {
+        sq += __shfl_xor(sq, 32);  // the partner lane holds the row's other 32 features
+        if (h == 0) {
+          ndelta[(size_t)head * N + qi] = -sq;
+          nlse[(size_t)head * N + qi] = -lse_i * inv_scale;
+        }
+      }
     }
   }
 }
@@ -315,7 +331,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
 
 hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o,
                            float* lse, int64_t heads, int64_t N, double scale, const Mask& mk,
-                           hipStream_t stream, const Timers& tm) {
+                           void* bwd_ws, hipStream_t stream, const Timers& tm) {
   const int nqb = (int)((N + kBr - 1) / kBr);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nqb);
   const float c = (float)(scale * 1.4426950408889634);  // scale * log2(e)
@@ -323,8 +339,11 @@ hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __
               : mk.causal ? attn_fwd_bf16_kernel<true, false>
                           : attn_fwd_bf16_kernel<false, false>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
+  // the backward workspace: -delta per row, then -lse / scale per row
+  float* ndelta = (float*)bwd_ws;
+  float* nlse = ndelta ? ndelta + heads * N : nullptr;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, (int)heads,
-                     (int)N, nqb, c, mk.band);
+                     (int)N, nqb, c, mk.band, ndelta, nlse, (float)(1.0 / scale));
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }

@@ -177,7 +177,7 @@ template <bool CAUSAL, bool BANDED>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale,
-    int band_arg) {
+    int band_arg, float* __restrict__ delta) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
   __shared__ Smem sm;
@@ -265,26 +265,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
     vnonfinite = __syncthreads_or(!fin);
   }
 
+  // epilogue; with delta given (the loss sum(o^2)/2, so dO = O) also the
+  // backward's per-row delta_i = |o_i|^2
   const float l = lsum + __shfl_xor(lsum, 32);
   const float inv = 1.0f / l;
   if (qi < N) {
+    float sq = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * dt + 8 * g + 4 * h;
-        *(float4*)(o + base + (size_t)qi * kD + d) =
-            make_float4(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv,
-                        oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+        const float4 x = make_float4(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv,
+                                     oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv);
+        *(float4*)(o + base + (size_t)qi * kD + d) = x;
+        sq = fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, fmaf(x.w, x.w, sq))));
       }
     if (h == 0) lse[(size_t)head * N + qi] = (mref + __log2f(l)) * kLn2;
+    if (delta) {
+      sq += __shfl_xor(sq, 32);  // the partner lane holds the row's other 32 features
+      if (h == 0) delta[(size_t)head * N + qi] = sq;
+    }
   }
 }
 
 }  // namespace
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int64_t heads, int64_t N, double scale, const Mask& mk,
+                          int64_t heads, int64_t N, double scale, const Mask& mk, void* bwd_ws,
                           hipStream_t stream, const Timers& tm) {
   const int nqb = (int)((N + kBr - 1) / kBr);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nqb);
@@ -294,7 +302,7 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           : attn_fwd_f32_kernel<false, false>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, (int)heads,
-                     (int)N, nqb, c, mk.band);
+                     (int)N, nqb, c, mk.band, (float*)bwd_ws);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }

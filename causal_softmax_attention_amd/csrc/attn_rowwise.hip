@@ -51,7 +51,8 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v, T* __restrict__ o,
                                                      acc_t<T>* __restrict__ lse, int N, int nqb,
-                                                     acc_t<T> scale, int causal, int band) {
+                                                     acc_t<T> scale, int causal, int band,
+                                                     acc_t<T>* __restrict__ delta) {
   using A = acc_t<T>;
   __shared__ A ks[kTile][kD];
   __shared__ A vs[kTile][kD];
@@ -101,9 +102,18 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
   }
   if (valid) {
     const A inv = A(1) / l;
+    A sq = 0;
 #pragma unroll
-    for (int f = 0; f < kF; ++f) o[base + (size_t)i * kD + f0 + f] = narrow<T>(acc[f] * inv);
+    for (int f = 0; f < kF; ++f) {
+      const T x = narrow<T>(acc[f] * inv);
+      o[base + (size_t)i * kD + f0 + f] = x;
+      sq += widen(x) * widen(x);
+    }
     if (g == 0) lse[(size_t)head * N + i] = m + log_acc(l);
+    if (delta) {  // the loss sum(o^2)/2: dO = O, so the backward's delta_i = |o_i|^2
+      sq = group_sum(sq);
+      if (g == 0) delta[(size_t)head * N + i] = sq;
+    }
   }
 }
 
@@ -247,13 +257,13 @@ __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
 
 template <typename T>
 hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64_t heads,
-                      int64_t N, double scale, const Mask& mk, hipStream_t stream,
+                      int64_t N, double scale, const Mask& mk, void* bwd_ws, hipStream_t stream,
                       const Timers& tm) {
   using A = acc_t<T>;
   const int nqb = (int)((N + kRows - 1) / kRows);
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
   hipLaunchKernelGGL(fwd_rowwise<T>, dim3((unsigned)(heads * nqb)), dim3(kThr), 0, stream, q, k,
-                     v, o, (A*)lse, (int)N, nqb, (A)scale, mk.causal, mk.band);
+                     v, o, (A*)lse, (int)N, nqb, (A)scale, mk.causal, mk.band, (A*)bwd_ws);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }
@@ -266,15 +276,17 @@ size_t bwd_workspace_bytes(int64_t heads, int64_t N) {
 template <typename T>
 hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* dout,
                       const void* lse, T* dq, T* dk, T* dv, void* workspace, int64_t heads,
-                      int64_t N, double scale, const Mask& mk, hipStream_t stream,
-                      const Timers& tm) {
+                      int64_t N, double scale, const Mask& mk, bool prepared,
+                      hipStream_t stream, const Timers& tm) {
   using A = acc_t<T>;
   A* delta = (A*)workspace;
   const int64_t rows = heads * N;
-  if (hipError_t e = mark(tm.start[kTimerBwdPre], stream)) return e;
-  hipLaunchKernelGGL(bwd_delta<T>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream, o,
-                     dout, delta, rows);
-  if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
+  if (!prepared) {  // else the forward already wrote delta (dO = O)
+    if (hipError_t e = mark(tm.start[kTimerBwdPre], stream)) return e;
+    hipLaunchKernelGGL(bwd_delta<T>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, stream,
+                       o, dout, delta, rows);
+    if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
+  }
   const int nb = (int)((N + kRows - 1) / kRows);
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
   hipLaunchKernelGGL(bwd_dkdv_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q,
@@ -290,11 +302,11 @@ hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* d
 
 #define ATTN_INSTANTIATE(T)                                                                     \
   template hipError_t launch_fwd<T>(const T*, const T*, const T*, T*, void*, int64_t, int64_t, \
-                                    double, const Mask&, hipStream_t, const Timers&);           \
+                                    double, const Mask&, void*, hipStream_t, const Timers&);    \
   template size_t bwd_workspace_bytes<T>(int64_t, int64_t);                                    \
   template hipError_t launch_bwd<T>(const T*, const T*, const T*, const T*, const T*,          \
                                     const void*, T*, T*, T*, void*, int64_t, int64_t, double,  \
-                                    const Mask&, hipStream_t, const Timers&);
+                                    const Mask&, bool, hipStream_t, const Timers&);
 ATTN_INSTANTIATE(double)
 ATTN_INSTANTIATE(float)  // the float32 backward (its forward runs on MFMA, attn_fwd_f32.hip)
 

@@ -28,12 +28,18 @@ struct Mask {
   int band = 0;
 };
 
+// Every forward launcher takes `bwd_ws`: null, or the backward workspace, which
+// the forward then fills with the per-row values of the loss sum(o^2)/2
+// (dO = O) so that the backward launchers can run `prepared` (without their
+// first, per-row kernel).  Layouts: bfloat16 -delta_i then -lse_i / scale
+// (float each); float32 / float64 delta_i in the accumulation type.
+
 // Row-per-group kernels (attn_rowwise.hip): forward and backward of `heads`
 // independent heads of N tokens, D = 64.  T is double or float; lse is double
 // for double, float otherwise.
 template <typename T>
 hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64_t heads,
-                      int64_t N, double scale, const Mask& mk, hipStream_t stream,
+                      int64_t N, double scale, const Mask& mk, void* bwd_ws, hipStream_t stream,
                       const Timers& tm);
 
 // Backward workspace bytes and launch (dq, dk, dv from q, k, v, o, dout, lse).
@@ -43,18 +49,18 @@ size_t bwd_workspace_bytes(int64_t heads, int64_t N);
 template <typename T>
 hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* dout,
                       const void* lse, T* dq, T* dk, T* dv, void* workspace, int64_t heads,
-                      int64_t N, double scale, const Mask& mk, hipStream_t stream,
-                      const Timers& tm);
+                      int64_t N, double scale, const Mask& mk, bool prepared,
+                      hipStream_t stream, const Timers& tm);
 
 // float32 forward on MFMA tiles (attn_fwd_f32.hip).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int64_t heads, int64_t N, double scale, const Mask& mk,
+                          int64_t heads, int64_t N, double scale, const Mask& mk, void* bwd_ws,
                           hipStream_t stream, const Timers& tm);
 
 // bfloat16 forward on MFMA tiles (attn_fwd_bf16.hip).
 hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __bf16* o,
                            float* lse, int64_t heads, int64_t N, double scale, const Mask& mk,
-                           hipStream_t stream, const Timers& tm);
+                           void* bwd_ws, hipStream_t stream, const Timers& tm);
 
 // bfloat16 backward on MFMA tiles (attn_bwd_bf16.hip); the workspace holds two floats
 // per row (-delta and -lse / scale).
@@ -62,13 +68,20 @@ size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N);
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
                            const __bf16* dout, const float* lse, __bf16* dq, __bf16* dk,
                            __bf16* dv, void* workspace, int64_t heads, int64_t N, double scale,
-                           const Mask& mk, hipStream_t stream, const Timers& tm);
+                           const Mask& mk, bool prepared, hipStream_t stream, const Timers& tm);
 
 // The dQ pass alone (attn_bwd_dq_bf16.hip), from the prep kernel's per-row values.
 hipError_t launch_bwd_dq_bf16(const __bf16* q, const __bf16* k, const __bf16* v,
                               const __bf16* dout, const float* nlse, const float* ndelta,
                               __bf16* dq, int64_t heads, int64_t N, double scale,
                               const Mask& mk, hipStream_t stream, const Timers& tm);
+
+// loss = sum(o^2)/2 from the per-row values a forward wrote (attn_loss.hip):
+// vals_kind 0 float64 delta, 1 float32 delta, 2 float32 -delta; `parts` holds
+// kLossParts doubles of scratch.
+constexpr int kLossParts = 256;
+hipError_t launch_loss(int vals_kind, const void* vals, int64_t rows, double* parts, double* loss,
+                       hipStream_t stream);
 
 hipError_t launch_nw(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,
                      const float* sx, const float* sy, const float* sv, float denom, float* out,

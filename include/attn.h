@@ -125,6 +125,27 @@ ATTN_API int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, dou
                       const void* o, const void* dout, const void* lse, void* dq, void* dk,
                       void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Training step of the pages' GRADIENT statement (loss = SUM(x * x) / 2 over
+ * every output value, so the upstream gradient is dout = o), with the loss
+ * fused into the forward:
+ * attn_fwd_train is attn_fwd that also
+ *   - writes *loss = sum(o^2) / 2 (one float64 in device memory, summed in a
+ *     fixed order from the stored o, so repeated calls give the same bits), and
+ *   - fills `workspace` (at least attn_bwd_workspace_bytes()) with the per-row
+ *     values the backward of that loss needs;
+ * attn_bwd_from_fwd is then attn_bwd(..., dout = o, ...) reading those values
+ * instead of recomputing them (one kernel fewer).  Pass it the same sizes,
+ * scale, mask, window, q, k, v, o, lse and workspace, unchanged in between.
+ * Returns ATTN_OK / ATTN_EINVAL / ATTN_EUNSUPPORTED / ATTN_EHIP. */
+ATTN_API int attn_fwd_train(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                            int mask, int64_t window, const void* q, const void* k,
+                            const void* v, void* o, void* lse, void* workspace,
+                            size_t workspace_bytes, double* loss, void* stream);
+ATTN_API int attn_bwd_from_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                               int mask, int64_t window, const void* q, const void* k,
+                               const void* v, const void* o, const void* lse, void* dq, void* dk,
+                               void* dv, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Nadaraya-Watson control (the pages' NADARAYA_WATSON query): for every target
  * p, out_p = sum_q w_pq v_q / sum_q w_pq over ALL sources q (a cross join),
  * w_pq = exp(-((tx_p - sx_q)^2 + (ty_p - sy_q)^2) / denom).  The pages use

@@ -31,6 +31,7 @@ def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["attn_causal_fwd", "attn_causal_bwd",
                                          "attn_causal_bwd_workspace_bytes", "attn_fwd",
                                          "attn_bwd", "attn_bwd_workspace_bytes",
+                                         "attn_fwd_train", "attn_bwd_from_fwd",
                                          "nw_gauss_average", "attn_set_kernel_timer",
                                          "attn_last_error"])
 
@@ -155,6 +156,41 @@ def test_masked_entry_points_check_sizes_first(L):
         assert mbwd(L, m, 4, scale=0.0) == csa.ATTN_EINVAL
     assert L.attn_bwd_workspace_bytes(2, 2, 3, 100, 64) == \
         L.attn_causal_bwd_workspace_bytes(2, 2, 3, 100, 64)
+
+
+def train_fwd(L, ws_bytes=None, loss=0x900000, ws=0x800000, **kw):
+    a = dict(dtype=2, B=1, H=1, N=16, D=64, scale=0.125, mask=0, window=0)
+    a.update(kw)
+    need = L.attn_bwd_workspace_bytes(a["dtype"], 1, 1, 16, 64)
+    return L.attn_fwd_train(a["dtype"], a["B"], a["H"], a["N"], a["D"], a["scale"], a["mask"],
+                            a["window"], P, P, P, ctypes.c_void_p(0x100000),
+                            ctypes.c_void_p(0x200000), ctypes.c_void_p(ws),
+                            need if ws_bytes is None else ws_bytes, ctypes.c_void_p(loss), None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(loss=0), csa.ATTN_EINVAL),                     # null loss
+    (dict(loss=0x900004), csa.ATTN_EINVAL),              # loss not 8-byte aligned
+    (dict(ws=0), csa.ATTN_EINVAL),                       # null workspace
+    (dict(ws_bytes=64), csa.ATTN_EINVAL),                # short workspace
+    (dict(ws=0x100000), csa.ATTN_EINVAL),                # workspace aliases o
+    (dict(loss=0x800000), csa.ATTN_EINVAL),              # loss inside the workspace
+    (dict(D=32), csa.ATTN_EUNSUPPORTED),
+    (dict(mask=2, window=0), csa.ATTN_EINVAL),
+])
+def test_fwd_train_rejects(L, kw, code):
+    assert train_fwd(L, **kw) == code
+    assert csa.attn_last_error() != ""
+
+
+def test_bwd_from_fwd_rejects(L):
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(9)]
+    need = L.attn_bwd_workspace_bytes(2, 1, 1, 16, 64)
+    call = lambda ws_bytes=need, ws=p[8], **kw: L.attn_bwd_from_fwd(
+        2, 1, 1, kw.get("N", 16), 64, 0.125, 0, 0, *p[:8], ws, ws_bytes, None)
+    assert call(ws_bytes=need - 1) == csa.ATTN_EINVAL
+    assert call(ws=ctypes.c_void_p(0)) == csa.ATTN_EINVAL
+    assert call(N=0) == csa.ATTN_EINVAL
 
 
 def test_nw_rejects(L):
