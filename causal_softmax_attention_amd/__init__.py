@@ -1,4 +1,6 @@
-"""Causal softmax attention (D = 64) and the Nadaraya-Watson control on MI355X.
+"""Causal softmax attention (D = 64) and the Nadaraya-Watson control on MI355X,
+with the steps before it: the long-table <-> matrix adapter and the Q / K / V
+input projections.
 
 A thin ctypes binding over the C ABI in ``include/attn.h`` (``libattn.so``,
 built in-tree by ``python -m causal_softmax_attention_amd._build``).  The
@@ -62,6 +64,16 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd_from_fwd.restype = ctypes.c_int
         L.nw_gauss_average.argtypes = [i64, vp, vp, i64, vp, vp, vp, ctypes.c_float, vp, vp]
         L.nw_gauss_average.restype = ctypes.c_int
+        L.attn_matrix_to_table.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp, vp, vp]
+        L.attn_matrix_to_table.restype = ctypes.c_int
+        L.attn_table_workspace_bytes.argtypes = [i64, i64]
+        L.attn_table_workspace_bytes.restype = sz
+        L.attn_table_to_matrix.argtypes = [ctypes.c_int, i64, vp, vp, vp, i64, i64, vp, vp, vp,
+                                           sz, vp]
+        L.attn_table_to_matrix.restype = ctypes.c_int
+        L.attn_qkv_project.argtypes = [ctypes.c_int, i64, i64, i64, i64, vp, vp, vp, vp, vp, vp,
+                                       vp, vp]
+        L.attn_qkv_project.restype = ctypes.c_int
         L.attn_set_kernel_timer.argtypes = [ctypes.c_int, vp, vp]
         L.attn_set_kernel_timer.restype = ctypes.c_int
         L.attn_last_error.argtypes = []
@@ -234,9 +246,83 @@ def nw_gauss_average(tx, ty, sx, sy, sv, denom: float = 0.25, out=None, stream=N
     return out
 
 
-TIMER_FWD, TIMER_BWD_PRE, TIMER_BWD_DKDV, TIMER_BWD_DQ, TIMER_NW = range(5)
+def _dev(t, name, dim):
+    if t.dim() != dim or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous {dim}-D device tensor")
+
+
+def attn_matrix_to_table(m, t=None, d=None, x=None, stream=None):
+    """The long table (t, d, x) of a [T, D] device matrix, rows in (t, d) order."""
+    import torch
+    _dev(m, "m", 2)
+    T, D = m.shape
+    t = torch.empty(T * D, dtype=torch.int64, device=m.device) if t is None else t
+    d = torch.empty(T * D, dtype=torch.int64, device=m.device) if d is None else d
+    x = torch.empty(T * D, dtype=m.dtype, device=m.device) if x is None else x
+    _check(lib().attn_matrix_to_table(_dtype_code(m), T, D, _ptr(m), _ptr(t), _ptr(d), _ptr(x),
+                                      _stream(m, stream)))
+    return t, d, x
+
+
+def attn_table_workspace_bytes(T: int, D: int) -> int:
+    return lib().attn_table_workspace_bytes(T, D)
+
+
+def attn_table_to_matrix(t, d, x, T: int, D: int, m=None, workspace=None, status=None,
+                         stream=None, check: bool = True):
+    """Pivot rows (t, d, x) into a [T, D] matrix (NaN where no row names a cell).
+
+    With check (the default) the call waits for the stream and raises ValueError
+    when a coordinate was out of range or a cell was named twice; without it,
+    returns (m, status) and the caller reads the int32 status word itself."""
+    import torch
+    for name, c in (("t", t), ("d", d), ("x", x)):
+        _dev(c, name, 1)
+    if t.dtype != torch.int64 or d.dtype != torch.int64:
+        raise ValueError("t and d must be int64")
+    if not (t.numel() == d.numel() == x.numel()):
+        raise ValueError("t, d and x must have one length")
+    m = torch.empty((T, D), dtype=x.dtype, device=x.device) if m is None else m
+    need = attn_table_workspace_bytes(T, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=x.device)
+    _check(lib().attn_table_to_matrix(_dtype_code(x), t.numel(), _ptr(t), _ptr(d), _ptr(x), T, D,
+                                      _ptr(m), _ptr(status), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream(x, stream)))
+    if not check:
+        return m, status
+    code = int(status.item())
+    if code:
+        what = [w for bit, w in ((1, "a coordinate is out of range"), (2, "a cell is named twice"))
+                if code & bit]
+        raise ValueError("table_to_matrix: " + " and ".join(what))
+    return m
+
+
+def attn_qkv_project(x, wq, wk, wv, heads: int, q=None, k=None, v=None, stream=None):
+    """(q, k, v) = (x Wq, x Wk, x Wv) laid out [B, heads, N, 64]; x is [B, N, Dm],
+    each weight [Dm, heads * 64]."""
+    import torch
+    _dev(x, "x", 3)
+    B, N, Dm = x.shape
+    for name, w in (("wq", wq), ("wk", wk), ("wv", wv)):
+        _dev(w, name, 2)
+        if tuple(w.shape) != (Dm, heads * 64) or w.dtype != x.dtype:
+            raise ValueError(f"{name} must be [{Dm}, {heads * 64}] of x's dtype")
+    outs = [torch.empty((B, heads, N, 64), dtype=x.dtype, device=x.device) if o is None else o
+            for o in (q, k, v)]
+    _check(lib().attn_qkv_project(_dtype_code(x), B, N, Dm, heads, _ptr(x), _ptr(wq), _ptr(wk),
+                                  _ptr(wv), *(_ptr(o) for o in outs), _stream(x, stream)))
+    return tuple(outs)
+
+
+TIMER_FWD, TIMER_BWD_PRE, TIMER_BWD_DKDV, TIMER_BWD_DQ, TIMER_NW, TIMER_TABLE, TIMER_PROJECT = range(7)
 TIMER_NAMES = {TIMER_FWD: "fwd", TIMER_BWD_PRE: "bwd_pre", TIMER_BWD_DKDV: "bwd_dkdv",
-               TIMER_BWD_DQ: "bwd_dq", TIMER_NW: "nw"}
+               TIMER_BWD_DQ: "bwd_dq", TIMER_NW: "nw", TIMER_TABLE: "table_to_matrix",
+               TIMER_PROJECT: "qkv_project"}
 
 
 def attn_set_kernel_timer(slot: int, start, stop):
@@ -248,5 +334,7 @@ def attn_set_kernel_timer(slot: int, start, stop):
 
 __all__ = ["attn_causal_fwd", "attn_causal_bwd", "attn_causal_bwd_workspace_bytes", "attn_fwd",
            "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_train", "attn_bwd_from_fwd", "MASKS",
-           "nw_gauss_average", "attn_set_kernel_timer", "attn_last_error", "lib", "AttnError",
+           "nw_gauss_average", "attn_matrix_to_table", "attn_table_to_matrix",
+           "attn_table_workspace_bytes", "attn_qkv_project", "attn_set_kernel_timer",
+           "attn_last_error", "lib", "AttnError",
            "ATTN_F64", "ATTN_F32", "ATTN_BF16"]

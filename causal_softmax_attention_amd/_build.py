@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["attn_api.hip", "attn_rowwise.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip",
-           "attn_bwd_dq_bf16.hip", "attn_fwd_f32.hip", "attn_loss.hip", "nw.hip"]
+           "attn_bwd_dq_bf16.hip", "attn_fwd_f32.hip", "attn_loss.hip", "nw.hip", "attn_table.hip",
+           "attn_project.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -45,6 +45,9 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 // element count must fit the int/int64 arithmetic used on the device.
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxHeads = int64_t(1) << 24;
+// Largest element count of a matrix, table or weight the adapter and the
+// projections index (int64 offsets; 2^40 elements is far beyond one GPU).
+constexpr int64_t kMaxCells = int64_t(1) << 40;
 
 int check_sizes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale) {
   if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16)
@@ -287,6 +290,96 @@ int nw_gauss_average(int64_t n_targets, const float* tx, const float* ty, int64_
   hipError_t e = attn::launch_nw(n_targets, tx, ty, n_sources, sx, sy, sv, denom, out,
                                  (hipStream_t)stream, g_tm);
   return hip_status(e, "nw_gauss_average launch");
+}
+
+size_t attn_table_workspace_bytes(int64_t T, int64_t D) {
+  if (T < 1 || D < 1 || T > kMaxCells / D) return 0;
+  return attn::table_workspace_bytes(T, D);
+}
+
+int attn_table_to_matrix(int dtype, int64_t rows, const int64_t* t, const int64_t* d,
+                         const void* x, int64_t T, int64_t D, void* m, int32_t* status,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_EINVAL, "unknown dtype %d", dtype);
+  if (rows < 1 || T < 1 || D < 1) return fail(ATTN_EINVAL, "rows, T and D must be >= 1");
+  if (T > kMaxCells / D || rows > kMaxCells)
+    return fail(ATTN_EINVAL, "at most %lld cells and rows", (long long)kMaxCells);
+  if (!t || !d || !x || !m || !status || !workspace)
+    return fail(ATTN_EINVAL, "null pointer argument");
+  const size_t es = elem_size(dtype);
+  if (((uintptr_t)t & 7u) || ((uintptr_t)d & 7u) || ((uintptr_t)x & (es - 1)) ||
+      ((uintptr_t)status & 3u) || !aligned16(m) || !aligned16(workspace))
+    return fail(ATTN_EINVAL, "misaligned pointer (t, d: 8; x: element; m, workspace: 16; status: 4)");
+  const size_t need = attn::table_workspace_bytes(T, D);
+  if (workspace_bytes < need)
+    return fail(ATTN_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
+                workspace_bytes, need);
+  const size_t ib = (size_t)rows * 8, xb = (size_t)rows * es, mb = (size_t)T * D * es;
+  if (overlap(m, mb, t, ib) || overlap(m, mb, d, ib) || overlap(m, mb, x, xb) ||
+      overlap(m, mb, workspace, need) || overlap(m, mb, status, 4))
+    return fail(ATTN_EINVAL, "the matrix must not alias an input, the workspace or the status");
+  if (overlap(workspace, need, t, ib) || overlap(workspace, need, d, ib) ||
+      overlap(workspace, need, x, xb) || overlap(workspace, need, status, 4))
+    return fail(ATTN_EINVAL, "the workspace must not alias an input or the status");
+  if (overlap(status, 4, t, ib) || overlap(status, 4, d, ib) || overlap(status, 4, x, xb))
+    return fail(ATTN_EINVAL, "the status must not alias an input");
+  return hip_status(attn::launch_table_to_matrix((int)es, rows, t, d, x, T, D, m, status,
+                                                 workspace, (hipStream_t)stream, g_tm),
+                    "attn_table_to_matrix launch");
+}
+
+int attn_matrix_to_table(int dtype, int64_t T, int64_t D, const void* m, int64_t* t, int64_t* d,
+                         void* x, void* stream) {
+  if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_EINVAL, "unknown dtype %d", dtype);
+  if (T < 1 || D < 1) return fail(ATTN_EINVAL, "T and D must be >= 1");
+  if (T > kMaxCells / D) return fail(ATTN_EINVAL, "at most %lld cells", (long long)kMaxCells);
+  if (!m || !t || !d || !x) return fail(ATTN_EINVAL, "null pointer argument");
+  const size_t es = elem_size(dtype);
+  if (((uintptr_t)t & 7u) || ((uintptr_t)d & 7u) || ((uintptr_t)x & (es - 1)) ||
+      ((uintptr_t)m & (es - 1)))
+    return fail(ATTN_EINVAL, "misaligned pointer (t, d: 8; m, x: element)");
+  const size_t cells = (size_t)T * D, ib = cells * 8, xb = cells * es;
+  if (overlap(t, ib, m, xb) || overlap(d, ib, m, xb) || overlap(x, xb, m, xb) ||
+      overlap(t, ib, d, ib) || overlap(t, ib, x, xb) || overlap(d, ib, x, xb))
+    return fail(ATTN_EINVAL, "t, d and x must not overlap each other or the matrix");
+  return hip_status(attn::launch_matrix_to_table((int)es, T, D, m, t, d, x, (hipStream_t)stream),
+                    "attn_matrix_to_table launch");
+}
+
+int attn_qkv_project(int dtype, int64_t B, int64_t N, int64_t Dm, int64_t H, const void* x,
+                     const void* wq, const void* wk, const void* wv, void* q, void* k, void* v,
+                     void* stream) {
+  if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_EINVAL, "unknown dtype %d", dtype);
+  if (B < 1 || N < 1 || Dm < 1 || H < 1)
+    return fail(ATTN_EINVAL, "sizes must be >= 1 (B=%lld N=%lld Dm=%lld H=%lld)", (long long)B,
+                (long long)N, (long long)Dm, (long long)H);
+  if (H > 65535) return fail(ATTN_EINVAL, "at most 65535 heads");
+  if (N > kMaxN || B > (int64_t(1) << 31) / N)
+    return fail(ATTN_EINVAL, "B*N must be below 2^31 and N at most %lld", (long long)kMaxN);
+  if (Dm > kMaxCells / (B * N) || Dm > kMaxCells / (H * 64))
+    return fail(ATTN_EINVAL, "x or a weight matrix exceeds %lld elements", (long long)kMaxCells);
+  if (!x || !wq || !wk || !wv || !q || !k || !v) return fail(ATTN_EINVAL, "null pointer argument");
+  const void* all[] = {x, wq, wk, wv, q, k, v};
+  for (const void* p : all)
+    if (!aligned16(p)) return fail(ATTN_EINVAL, "pointers must be 16-byte aligned");
+  const size_t es = elem_size(dtype);
+  const size_t xb = (size_t)B * N * Dm * es, wb = (size_t)Dm * H * 64 * es,
+               ob = (size_t)B * H * N * 64 * es;
+  const void* ins[] = {wq, wk, wv};
+  void* outs[] = {q, k, v};
+  for (void* o : outs) {
+    if (overlap(o, ob, x, xb)) return fail(ATTN_EINVAL, "outputs must not alias inputs");
+    for (const void* w : ins)
+      if (overlap(o, ob, w, wb)) return fail(ATTN_EINVAL, "outputs must not alias inputs");
+  }
+  if (overlap(q, ob, k, ob) || overlap(q, ob, v, ob) || overlap(k, ob, v, ob))
+    return fail(ATTN_EINVAL, "q, k and v must not overlap");
+  return hip_status(attn::launch_project((int)es, B, N, Dm, H, x, wq, wk, wv, q, k, v,
+                                         (hipStream_t)stream, g_tm),
+                    "attn_qkv_project launch");
 }
 
 int attn_set_kernel_timer(int slot, void* start, void* stop) {

@@ -11,10 +11,18 @@ namespace attn {
 // Caller-supplied timing events, one start/stop pair per kernel slot
 // (ATTN_TIMER_* in include/attn.h); null events are skipped.
 struct Timers {
-  hipEvent_t start[5] = {};
-  hipEvent_t stop[5] = {};
+  hipEvent_t start[7] = {};
+  hipEvent_t stop[7] = {};
 };
-enum { kTimerFwd = 0, kTimerBwdPre = 1, kTimerBwdDkdv = 2, kTimerBwdDq = 3, kTimerNw = 4 };
+enum {
+  kTimerFwd = 0,
+  kTimerBwdPre = 1,
+  kTimerBwdDkdv = 2,
+  kTimerBwdDq = 3,
+  kTimerNw = 4,
+  kTimerTable = 5,
+  kTimerProject = 6
+};
 
 inline hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
 
@@ -86,5 +94,19 @@ hipError_t launch_loss(int vals_kind, const void* vals, int64_t rows, double* pa
 hipError_t launch_nw(int64_t n_targets, const float* tx, const float* ty, int64_t n_sources,
                      const float* sx, const float* sy, const float* sv, float denom, float* out,
                      hipStream_t stream, const Timers& tm);
+
+// Long-table <-> matrix adapter (attn_table.hip).  elem_bytes: 8, 4 or 2.
+size_t table_workspace_bytes(int64_t T, int64_t D);
+hipError_t launch_table_to_matrix(int elem_bytes, int64_t rows, const int64_t* t, const int64_t* d,
+                                  const void* x, int64_t T, int64_t D, void* out, int32_t* status,
+                                  void* workspace, hipStream_t stream, const Timers& tm);
+hipError_t launch_matrix_to_table(int elem_bytes, int64_t T, int64_t D, const void* m, int64_t* t,
+                                  int64_t* d, void* x, hipStream_t stream);
+
+// Q / K / V input projections (attn_project.hip).  elem_bytes: 8, 4 or 2.
+bool project_uses_mfma(int elem_bytes, int64_t M, int64_t Dm, int64_t H);
+hipError_t launch_project(int elem_bytes, int64_t B, int64_t N, int64_t Dm, int64_t H,
+                          const void* x, const void* wq, const void* wk, const void* wv, void* q,
+                          void* k, void* v, hipStream_t stream, const Timers& tm);
 
 }  // namespace attn

@@ -22,7 +22,15 @@ bf16_4k       2  (8, 32, 4096, 64)       q, k, v ~ N(0, 1) -> bfloat16
 nw_64k        3  65,536 x 65,536         targets, sources ~ U[0, 10)^2,
                                          v = sin(x)cos(y) + 0.1 N(0, 1)
 bf16_32k      4  (1, 16, 32768, 64)      q, k ~ 2 N(0, 1), v ~ N(0, 1) -> bf16
+proj_4k       5  x (8, 4096, 2048),      x ~ N(0, 1); wq, wk, wv ~ N(0, 1/2048)
+                 w (2048, 32 * 64)       -> bfloat16 (Q, K, V of bf16_4k's shape)
+table_16x32k  6  (524288, 64) matrix     m ~ N(0, 1) -> bfloat16; its 2^25 rows
+                                         (t, d, x) in a seeded random order
 =========  ====  ======================  =====================================
+
+The projection draws follow the page on MLIR attention heads (x, then Wq, Wk,
+Wv); weights are scaled by 1/sqrt(d_model) so the projected values are of
+order one, as the attention inputs above are.
 """
 from __future__ import annotations
 
@@ -148,3 +156,50 @@ def page_nw_inputs() -> NWInputs:
     y = np.sin(4 * sources[:, 0]) + np.cos(3 * sources[:, 1])
     return NWInputs(targets[:, 0].copy(), targets[:, 1].copy(),
                     sources[:, 0].copy(), sources[:, 1].copy(), y)
+
+
+@dataclass
+class ProjectionInputs:
+    """x [B, N, Dm] and wq, wk, wv [Dm, H * 64] in the storage format of dtype
+    (uint16 bit patterns for "bf16"), with ``as_f64`` as for AttentionInputs."""
+
+    dtype: str
+    heads: int
+    x: np.ndarray
+    wq: np.ndarray
+    wk: np.ndarray
+    wv: np.ndarray
+
+    def as_f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if self.dtype == "bf16":
+            return bf16_bits_to_f32(a).astype(np.float64)
+        return a.astype(np.float64)
+
+
+def projection_inputs(seed: int, B: int, N: int, Dm: int, H: int, dtype: str) -> ProjectionInputs:
+    """x ~ N(0, 1) [B, N, Dm], then wq, wk, wv ~ N(0, 1/Dm) [Dm, H * 64]."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(B, N, Dm))
+    ws = [rng.normal(size=(Dm, H * D)) / np.sqrt(Dm) for _ in range(3)]
+    return ProjectionInputs(dtype, H, cast(x, dtype), *(cast(w, dtype) for w in ws))
+
+
+PROJECTION_WORKLOADS = {"proj_4k": (5, 8, 4096, 2048, 32, "bf16")}
+
+
+def projection_workload(name: str) -> ProjectionInputs:
+    seed, B, N, Dm, H, dtype = PROJECTION_WORKLOADS[name]
+    return projection_inputs(seed, B, N, Dm, H, dtype)
+
+
+def table_matrix(seed: int, T: int, Dc: int, dtype: str):
+    """A T x Dc matrix ~ N(0, 1) in the storage format of dtype, and a
+    permutation of its T * Dc cells (the order its table rows arrive in)."""
+    rng = np.random.default_rng(seed)
+    m = cast(rng.normal(size=(T, Dc)), dtype)
+    perm = rng.permutation(T * Dc)
+    return m, perm
+
+
+TABLE_WORKLOADS = {"table_16x32k": (6, 16 * 32768, 64, "bf16")}

@@ -157,10 +157,61 @@ ATTN_API int nw_gauss_average(int64_t n_targets, const float* tx, const float* t
                      const float* sx, const float* sy, const float* sv, float denom,
                      float* out, void* stream);
 
+/* ---- Steps before the path ------------------------------------------------
+ *
+ * The long table <-> matrix adapter (pages: "Show HN: automatic deduction of
+ * FlashAttention kernel from 25 lines of SQL", the demo script's helpers
+ * table() and matrix()).  The SQL engines hold a T x D matrix as the long
+ * table (t, d, x): one row per cell, t and d its row and column positions.
+ * Columns are separate arrays: t[rows], d[rows] (int64) and x[rows] (the
+ * element type `dtype`).  The matrix is dense row-major [T, D] of `dtype`.
+ *
+ * attn_matrix_to_table: the T*D rows of matrix m in (t, d) order (row
+ *   r = t*D + d), the order of the forward's ORDER BY t, d.  Values are copied
+ *   bit for bit.  Alignment: t, d 8 bytes; m, x one element.  The outputs must
+ *   not overlap each other or m.
+ *
+ * attn_table_to_matrix: the pivot.  Cell (t, d) of m receives the x of the row
+ *   naming it, bit for bit; a cell no row names is a quiet NaN.  A row whose
+ *   coordinate lies outside [0, T) x [0, D) is skipped, and a cell named by
+ *   two rows is an error: the call writes to the device word *status 0 when
+ *   neither happened, else the OR of 1 (some coordinate out of range) and 2
+ *   (some cell named twice), in which case m is unspecified.  The caller reads
+ *   *status after synchronising the stream.  `workspace` holds
+ *   attn_table_workspace_bytes(T, D) bytes of scratch (one counter per cell).
+ *   Alignment: t, d 8 bytes; x one element; m and workspace 16 bytes;
+ *   status 4 bytes.  m, the workspace and status must not overlap the inputs
+ *   or each other.  At most 2^40 rows and 2^40 cells (ATTN_EINVAL).
+ *   attn_table_workspace_bytes returns 0 for sizes the call would reject. */
+ATTN_API int attn_matrix_to_table(int dtype, int64_t T, int64_t D, const void* m, int64_t* t,
+                                  int64_t* d, void* x, void* stream);
+ATTN_API size_t attn_table_workspace_bytes(int64_t T, int64_t D);
+ATTN_API int attn_table_to_matrix(int dtype, int64_t rows, const int64_t* t, const int64_t* d,
+                                  const void* x, int64_t T, int64_t D, void* m, int32_t* status,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* The query, key and value input projections (pages: the "Wiki notes" page,
+ * brainpick-2k7.pages.dev, its MLIR functions @attention_head and
+ * @mini_attention: Q = x Wq, K = x Wk, V = x Wv).  x is [B, N, Dm] (one
+ * embedding row per token); each weight is [Dm, H*64] with head h in columns
+ * 64h .. 64h+63 (no bias, no scale).  q, k, v are written as the attention
+ * takes them, [B, H, N, 64]:  q[b][h][n][j] = sum_c x[b][n][c] wq[c][64h + j].
+ * One launch forms all three from one read of x.  Arithmetic: float64 for
+ * ATTN_F64, float32 for ATTN_F32; ATTN_BF16 multiplies bfloat16 operands
+ * with float32 accumulation and rounds the results to bfloat16 (nearest even).
+ * All pointers 16-byte aligned; the outputs must not overlap each other or
+ * the inputs.  Limits (ATTN_EINVAL): sizes >= 1, H <= 65535, B*N < 2^31,
+ * N <= 2^24, x and each weight at most 2^40 elements. */
+ATTN_API int attn_qkv_project(int dtype, int64_t B, int64_t N, int64_t Dm, int64_t H,
+                              const void* x, const void* wq, const void* wk, const void* wv,
+                              void* q, void* k, void* v, void* stream);
+
 /* Profiling hook: timing events around one kernel.  Kernels are named by
  * slot: ATTN_TIMER_FWD (the forward kernel), ATTN_TIMER_BWD_PRE (the
  * backward's per-row delta kernel), ATTN_TIMER_BWD_DKDV (dK/dV), ATTN_TIMER_BWD_DQ
- * (dQ), ATTN_TIMER_NW (the Nadaraya-Watson kernel).  While a slot is set (per
+ * (dQ), ATTN_TIMER_NW (the Nadaraya-Watson kernel), ATTN_TIMER_TABLE (the
+ * pivot's scatter kernel of attn_table_to_matrix), ATTN_TIMER_PROJECT (the
+ * kernel of attn_qkv_project).  While a slot is set (per
  * host thread), each call that launches that kernel records `start` on its
  * stream just before the launch and `stop` just after it, so hipEventElapsedTime
  * gives the kernel's duration.  Both are hipEvent_t created by the caller; pass
@@ -172,7 +223,9 @@ enum {
   ATTN_TIMER_BWD_DKDV = 2,
   ATTN_TIMER_BWD_DQ = 3,
   ATTN_TIMER_NW = 4,
-  ATTN_TIMER_SLOTS = 5
+  ATTN_TIMER_TABLE = 5,
+  ATTN_TIMER_PROJECT = 6,
+  ATTN_TIMER_SLOTS = 7
 };
 ATTN_API int attn_set_kernel_timer(int slot, void* start, void* stop);
 

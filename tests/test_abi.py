@@ -33,7 +33,9 @@ def test_header_declares_the_entry_points():
                                          "attn_bwd", "attn_bwd_workspace_bytes",
                                          "attn_fwd_train", "attn_bwd_from_fwd",
                                          "nw_gauss_average", "attn_set_kernel_timer",
-                                         "attn_last_error"])
+                                         "attn_last_error", "attn_matrix_to_table",
+                                         "attn_table_workspace_bytes", "attn_table_to_matrix",
+                                         "attn_qkv_project"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -208,8 +210,67 @@ def test_nw_rejects(L):
 
 def test_timer_hook(L):
     assert L.attn_set_kernel_timer(0, P, None) == csa.ATTN_EINVAL
-    assert L.attn_set_kernel_timer(5, None, None) == csa.ATTN_EINVAL
+    assert L.attn_set_kernel_timer(7, None, None) == csa.ATTN_EINVAL
     assert L.attn_set_kernel_timer(-1, None, None) == csa.ATTN_EINVAL
-    for slot in range(5):
+    for slot in range(7):
         assert L.attn_set_kernel_timer(slot, None, None) == csa.ATTN_OK
     assert csa.attn_last_error() == ""
+
+
+def _addr(i):
+    return ctypes.c_void_p(0x1000000 * (i + 1))
+
+
+def test_matrix_to_table_rejects(L):
+    m, t, d, x = (_addr(i) for i in range(4))
+    call = lambda dtype=2, T=4, D=8, m=m, t=t, d=d, x=x: L.attn_matrix_to_table(
+        dtype, T, D, m, t, d, x, None)
+    assert call(dtype=5) == csa.ATTN_EINVAL
+    assert call(T=0) == csa.ATTN_EINVAL
+    assert call(D=-2) == csa.ATTN_EINVAL
+    assert call(T=1 << 30, D=1 << 20) == csa.ATTN_EINVAL          # over 2^40 cells
+    assert call(t=ctypes.c_void_p(0)) == csa.ATTN_EINVAL
+    assert call(d=ctypes.c_void_p(0x1000004)) == csa.ATTN_EINVAL  # int64 column misaligned
+    assert call(x=ctypes.c_void_p(0x3000001)) == csa.ATTN_EINVAL  # bf16 misaligned
+    assert call(x=t) == csa.ATTN_EINVAL                           # outputs overlap
+    assert call(t=m) == csa.ATTN_EINVAL                           # output overlaps the matrix
+
+
+def test_table_workspace_bytes(L):
+    assert L.attn_table_workspace_bytes(4, 8) == 4 * 8 * 4
+    assert L.attn_table_workspace_bytes(0, 8) == 0
+    assert L.attn_table_workspace_bytes(1 << 30, 1 << 20) == 0
+
+
+def test_table_to_matrix_rejects(L):
+    t, d, x, m, st, ws = (_addr(i) for i in range(6))
+    need = L.attn_table_workspace_bytes(4, 8)
+    call = lambda dtype=1, rows=32, t=t, d=d, x=x, T=4, D=8, m=m, st=st, ws=ws, wb=need: \
+        L.attn_table_to_matrix(dtype, rows, t, d, x, T, D, m, st, ws, wb, None)
+    assert call(dtype=9) == csa.ATTN_EINVAL
+    assert call(rows=0) == csa.ATTN_EINVAL
+    assert call(T=0) == csa.ATTN_EINVAL
+    assert call(wb=need - 1) == csa.ATTN_EINVAL
+    assert call(st=ctypes.c_void_p(0)) == csa.ATTN_EINVAL
+    assert call(ws=ctypes.c_void_p(0x6000008)) == csa.ATTN_EINVAL  # workspace not 16-aligned
+    assert call(m=ctypes.c_void_p(0x5000004)) == csa.ATTN_EINVAL   # matrix not 16-aligned
+    assert call(st=ctypes.c_void_p(0x5000002)) == csa.ATTN_EINVAL  # status misaligned
+    assert call(m=x) == csa.ATTN_EINVAL                            # matrix aliases x
+    assert call(ws=t) == csa.ATTN_EINVAL                           # workspace aliases t
+    assert call(st=d) == csa.ATTN_EINVAL                           # status aliases d
+
+
+def test_qkv_project_rejects(L):
+    x, wq, wk, wv, q, k, v = (_addr(i) for i in range(7))
+    call = lambda dtype=2, B=1, N=16, Dm=64, H=1, ptrs=(x, wq, wk, wv, q, k, v): \
+        L.attn_qkv_project(dtype, B, N, Dm, H, *ptrs, None)
+    assert call(dtype=3) == csa.ATTN_EINVAL
+    assert call(B=0) == csa.ATTN_EINVAL
+    assert call(Dm=0) == csa.ATTN_EINVAL
+    assert call(H=70000) == csa.ATTN_EINVAL
+    assert call(B=1 << 20, N=1 << 12) == csa.ATTN_EINVAL            # B*N >= 2^31
+    assert call(ptrs=(x, wq, wk, wv, q, k, ctypes.c_void_p(0))) == csa.ATTN_EINVAL
+    assert call(ptrs=(x, wq, wk, ctypes.c_void_p(0x4000008), q, k, v)) == csa.ATTN_EINVAL
+    assert call(ptrs=(x, wq, wk, wv, x, k, v)) == csa.ATTN_EINVAL   # q aliases x
+    assert call(ptrs=(x, wq, wk, wv, q, q, v)) == csa.ATTN_EINVAL   # k overlaps q
+    assert "overlap" in csa.attn_last_error()

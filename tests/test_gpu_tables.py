@@ -1,0 +1,143 @@
+"""GPU parity for the long-table <-> matrix adapter (attn_matrix_to_table,
+attn_table_to_matrix) against the oracle's table() / matrix().  Index and byte
+work: every comparison is bit-exact (t, d as integers; values as raw bits,
+holes as the element type's quiet NaN)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import causal_softmax_attention_amd.inputs as inp  # noqa: E402
+from oracle import tables  # noqa: E402
+from gpu_util import DEV, note  # noqa: E402
+
+NP_BITS = {"f64": np.uint64, "f32": np.uint32, "bf16": np.uint16}
+TORCH_BITS = {"f64": torch.int64, "f32": torch.int32, "bf16": torch.int16}
+TORCH_DT = {"f64": torch.float64, "f32": torch.float32, "bf16": torch.bfloat16}
+NAN_BITS = {"f64": 0x7FF8000000000000, "f32": 0x7FC00000, "bf16": 0x7FC0}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import causal_softmax_attention_amd as csa
+    csa.lib()
+
+
+def _values(seed, T, D, dtype):
+    """Storage-format values (bit patterns for bf16) with special values mixed in."""
+    m, _ = inp.table_matrix(seed, T, D, dtype)
+    flat = m.reshape(-1)
+    if dtype == "bf16":
+        specials = np.array([0x8000, 0x7F80, 0xFF80, 0x0001, 0x0080], dtype=np.uint16)
+    else:
+        ft = np.float64 if dtype == "f64" else np.float32
+        specials = np.array([-0.0, np.inf, -np.inf, np.finfo(ft).tiny / 4, np.finfo(ft).tiny],
+                            dtype=ft)
+    k = min(flat.size, specials.size)
+    flat[:k] = specials[:k]
+    return m
+
+
+def _to_dev(a, dtype):
+    return torch.from_numpy(np.ascontiguousarray(a).view(NP_BITS[dtype]).view(
+        {"f64": np.int64, "f32": np.int32, "bf16": np.int16}[dtype])).to(DEV).view(TORCH_DT[dtype])
+
+
+def _bits(t, dtype):
+    return t.view(TORCH_BITS[dtype]).cpu().numpy().view(NP_BITS[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
+@pytest.mark.parametrize("T,D", [(1, 1), (3, 64), (257, 65), (64, 64), (5, 3)])
+def test_matrix_to_table(dtype, T, D):
+    import causal_softmax_attention_amd as csa
+    m = _values(30 + T + D, T, D, dtype)
+    note(f"matrix_to_table {dtype} {T}x{D}")
+    t, d, x = csa.attn_matrix_to_table(_to_dev(m, dtype))
+    torch.cuda.synchronize()
+    wt, wd, wx = tables.table(m.view(NP_BITS[dtype]))
+    assert np.array_equal(t.cpu().numpy(), wt) and np.array_equal(d.cpu().numpy(), wd)
+    assert np.array_equal(_bits(x, dtype), wx)
+
+
+@pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
+@pytest.mark.parametrize("T,D,holes", [(1, 1, 0), (3, 64, 0), (257, 65, 0), (64, 64, 37),
+                                       (9, 7, 5)])
+def test_table_to_matrix(dtype, T, D, holes):
+    """Rows in a shuffled order, some cells left out: the pivot equals the
+    oracle's bit for bit (oracle on the raw bit patterns, holes = NaN bits)."""
+    import causal_softmax_attention_amd as csa
+    m = _values(40 + T + D, T, D, dtype)
+    t, d, x = tables.table(m.view(NP_BITS[dtype]))
+    rng = np.random.default_rng(T * 100 + D)
+    keep = rng.permutation(t.size)[: t.size - holes]
+    t, d, x = t[keep], d[keep], x[keep]
+    note(f"table_to_matrix {dtype} {T}x{D} holes={holes}")
+    got = csa.attn_table_to_matrix(torch.from_numpy(t).to(DEV), torch.from_numpy(d).to(DEV),
+                                   _to_dev(x, dtype), T, D)
+    torch.cuda.synchronize()
+    # the oracle pivots the row numbers (exact in float64); a cell it leaves
+    # NaN is a hole, any other holds the bits of the row it names
+    src = tables.matrix(t, d, np.arange(t.size, dtype=np.float64), T, D)
+    hole = np.isnan(src)
+    assert hole.sum() == holes
+    gb = _bits(got, dtype)
+    assert np.all(gb[hole] == NAN_BITS[dtype])
+    assert np.array_equal(gb[~hole], x[src[~hole].astype(np.int64)])
+
+
+@pytest.mark.parametrize("case,code", [("dup", 2), ("range", 1), ("both", 3)])
+def test_table_to_matrix_status(case, code):
+    """A cell named twice or a coordinate out of range: the oracle raises, the
+    library sets the matching status bits (and the binding raises)."""
+    import causal_softmax_attention_amd as csa
+    T, D = 6, 5
+    t, d, x = tables.table(np.arange(T * D, dtype=np.float32).reshape(T, D))
+    if case in ("dup", "both"):
+        d = d.copy(); d[7] = d[8]; t = t.copy(); t[7] = t[8]
+    if case in ("range", "both"):
+        t = t.copy(); t[3] = T
+    with pytest.raises(ValueError):
+        tables.matrix(t, d, x, T, D)
+    note(f"table_to_matrix status {case}")
+    td, dd, xd = (torch.from_numpy(a).to(DEV) for a in (t, d, x))
+    _, status = csa.attn_table_to_matrix(td, dd, xd, T, D, check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == code
+    with pytest.raises(ValueError):
+        csa.attn_table_to_matrix(td, dd, xd, T, D)
+    # a clean call on the same status word clears it
+    _, status2 = csa.attn_table_to_matrix(*(torch.from_numpy(a).to(DEV)
+                                            for a in tables.table(np.ones((T, D), np.float32))),
+                                          T, D, status=status, check=False)
+    torch.cuda.synchronize()
+    assert int(status2.item()) == 0
+
+
+def test_table_workload_round_trip():
+    """The bench workload: a 524288 x 64 bfloat16 matrix (16 heads of 32768
+    tokens), its 2^25 rows in a seeded random order, pivoted back.  The whole
+    result equals the original bit for bit; the oracle's pivot of a sampled
+    stretch of the shuffled rows agrees cell by cell."""
+    import causal_softmax_attention_amd as csa
+    seed, T, D, dtype = inp.TABLE_WORKLOADS["table_16x32k"]
+    m, perm = inp.table_matrix(seed, T, D, dtype)
+    note(f"table workload {T}x{D}")
+    md = _to_dev(m, dtype)
+    t, d, x = csa.attn_matrix_to_table(md)
+    p = torch.from_numpy(perm).to(DEV)
+    got = csa.attn_table_to_matrix(t[p], d[p], x[p], T, D)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), md.view(torch.int16))
+    # oracle on 20000 of the shuffled rows, pivoted into a T x D matrix of holes
+    sel = perm[:20000]
+    ts, ds = sel // D, sel % D
+    want = tables.matrix(ts, ds, m.reshape(-1)[sel].astype(np.float64), T, D)
+    gb = _bits(got, dtype).reshape(-1)
+    assert np.array_equal(gb[sel], want.reshape(-1)[sel].astype(np.uint16))
