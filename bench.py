@@ -194,7 +194,8 @@ def cpu_baseline(a, budget_s=10.0):
 
 
 def secondary(steps):
-    """Other workloads: fp32 forward, long-sequence bf16 fwd+bwd, NW control, fp64 latency."""
+    """Other workloads: fp32 forward, long-sequence bf16 fwd+bwd, other join
+    predicates, fp64 latency, the NW control, and the steps before the path."""
     import numpy as np
     import torch
 
@@ -258,6 +259,77 @@ def secondary(steps):
     out["nw_64k"] = {"ms": ms, "Gpairs/s": 65536.0 ** 2 / ms / 1e6,
                      "alu_bound_Gpairs/s": nw_bound,
                      "frac_of_alu_bound": 65536.0 ** 2 / ms / 1e6 / nw_bound}
+    del cols, res
+    out.update(steps_before_the_path(steps))
+    return out
+
+
+def _mean_ms(call, steps, warmup=2):
+    """Mean wall time of one call on the current stream, HIP events around `steps` calls."""
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        call()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / steps
+
+
+def steps_before_the_path(steps):
+    """The fused Q/K/V projection producing the bf16_4k inputs, and the long-table
+    adapter on a 2^25-row bf16 table (16 heads of 32768 tokens)."""
+    import numpy as np
+    import torch
+
+    import causal_softmax_attention_amd as csa
+    import causal_softmax_attention_amd.inputs as inp
+    dev = "cuda:0"
+    bits = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    out = {}
+    _, B_, N_, Dm_, H_, _ = inp.PROJECTION_WORKLOADS["proj_4k"]
+    pa = inp.projection_workload("proj_4k")
+    xw = [bits(getattr(pa, n)) for n in ("x", "wq", "wk", "wv")]
+    qkv = [torch.empty((B_, H_, N_, D), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    ms = _mean_ms(lambda: csa.attn_qkv_project(*xw, H_, *qkv), steps)
+    fl = 3 * 2 * B_ * N_ * Dm_ * H_ * D
+    out["qkv_project_4k"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
+                             "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
+                             "shape": f"x [{B_}, {N_}, {Dm_}] -> q, k, v [{B_}, {H_}, {N_}, 64]"}
+    del xw, qkv, pa
+    seed, T_, D2, _ = inp.TABLE_WORKLOADS["table_16x32k"]
+    m, perm = inp.table_matrix(seed, T_, D2, "bf16")
+    md = bits(m)
+    t, d, x = csa.attn_matrix_to_table(md)
+    p = torch.from_numpy(perm).to(dev)
+    ts, ds, xs = t[p], d[p], x[p]
+    del p
+    mat = torch.empty_like(md)
+    ws = torch.empty(csa.attn_table_workspace_bytes(T_, D2), dtype=torch.uint8, device=dev)
+    st = torch.empty(1, dtype=torch.int32, device=dev)
+    ms = _mean_ms(lambda: csa.attn_table_to_matrix(ts, ds, xs, T_, D2, m=mat, workspace=ws,
+                                                   status=st, check=False), steps)
+    cells = T_ * D2
+    algo = cells * (8 + 8 + 2) + cells * 2          # read t, d, x; write the matrix
+    out["table_to_matrix_16x32k"] = {"ms": ms, "Mrows/s": cells / ms / 1e3,
+                                     "GB/s": algo / ms / 1e6,
+                                     "frac_of_hbm": algo / ms / 1e6 / HBM_PEAK,
+                                     "algorithmic_bytes": algo,
+                                     "status": int(st.item())}
+    # the same rows in (t, d) order, as the forward's ORDER BY t, d returns them
+    ms = _mean_ms(lambda: csa.attn_table_to_matrix(t, d, x, T_, D2, m=mat, workspace=ws,
+                                                   status=st, check=False), steps)
+    out["table_to_matrix_16x32k_ordered"] = {"ms": ms, "GB/s": algo / ms / 1e6,
+                                             "frac_of_hbm": algo / ms / 1e6 / HBM_PEAK,
+                                             "status": int(st.item())}
+    ms = _mean_ms(lambda: csa.attn_matrix_to_table(md, t=t, d=d, x=x), steps)
+    algo = cells * 2 + cells * (8 + 8 + 2)          # read the matrix; write t, d, x
+    out["matrix_to_table_16x32k"] = {"ms": ms, "GB/s": algo / ms / 1e6,
+                                     "frac_of_hbm": algo / ms / 1e6 / HBM_PEAK,
+                                     "algorithmic_bytes": algo}
     return out
 
 

@@ -337,9 +337,8 @@ int attn_matrix_to_table(int dtype, int64_t T, int64_t D, const void* m, int64_t
   if (T > kMaxCells / D) return fail(ATTN_EINVAL, "at most %lld cells", (long long)kMaxCells);
   if (!m || !t || !d || !x) return fail(ATTN_EINVAL, "null pointer argument");
   const size_t es = elem_size(dtype);
-  if (((uintptr_t)t & 7u) || ((uintptr_t)d & 7u) || ((uintptr_t)x & (es - 1)) ||
-      ((uintptr_t)m & (es - 1)))
-    return fail(ATTN_EINVAL, "misaligned pointer (t, d: 8; m, x: element)");
+  if (!aligned16(t) || !aligned16(d) || !aligned16(x) || !aligned16(m))
+    return fail(ATTN_EINVAL, "pointers must be 16-byte aligned");
   const size_t cells = (size_t)T * D, ib = cells * 8, xb = cells * es;
   if (overlap(t, ib, m, xb) || overlap(d, ib, m, xb) || overlap(x, xb, m, xb) ||
       overlap(t, ib, d, ib) || overlap(t, ib, x, xb) || overlap(d, ib, x, xb))

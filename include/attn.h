@@ -168,8 +168,8 @@ ATTN_API int nw_gauss_average(int64_t n_targets, const float* tx, const float* t
  *
  * attn_matrix_to_table: the T*D rows of matrix m in (t, d) order (row
  *   r = t*D + d), the order of the forward's ORDER BY t, d.  Values are copied
- *   bit for bit.  Alignment: t, d 8 bytes; m, x one element.  The outputs must
- *   not overlap each other or m.
+ *   bit for bit.  All four pointers 16-byte aligned.  The outputs must not
+ *   overlap each other or m.
  *
  * attn_table_to_matrix: the pivot.  Cell (t, d) of m receives the x of the row
  *   naming it, bit for bit; a cell no row names is a quiet NaN.  A row whose
@@ -178,7 +178,7 @@ ATTN_API int nw_gauss_average(int64_t n_targets, const float* tx, const float* t
  *   neither happened, else the OR of 1 (some coordinate out of range) and 2
  *   (some cell named twice), in which case m is unspecified.  The caller reads
  *   *status after synchronising the stream.  `workspace` holds
- *   attn_table_workspace_bytes(T, D) bytes of scratch (one counter per cell).
+ *   attn_table_workspace_bytes(T, D) bytes of scratch (one bit per cell).
  *   Alignment: t, d 8 bytes; x one element; m and workspace 16 bytes;
  *   status 4 bytes.  m, the workspace and status must not overlap the inputs
  *   or each other.  At most 2^40 rows and 2^40 cells (ATTN_EINVAL).

@@ -230,14 +230,15 @@ def test_matrix_to_table_rejects(L):
     assert call(D=-2) == csa.ATTN_EINVAL
     assert call(T=1 << 30, D=1 << 20) == csa.ATTN_EINVAL          # over 2^40 cells
     assert call(t=ctypes.c_void_p(0)) == csa.ATTN_EINVAL
-    assert call(d=ctypes.c_void_p(0x1000004)) == csa.ATTN_EINVAL  # int64 column misaligned
-    assert call(x=ctypes.c_void_p(0x3000001)) == csa.ATTN_EINVAL  # bf16 misaligned
+    assert call(d=ctypes.c_void_p(0x1000008)) == csa.ATTN_EINVAL  # not 16-byte aligned
+    assert call(x=ctypes.c_void_p(0x3000002)) == csa.ATTN_EINVAL  # not 16-byte aligned
     assert call(x=t) == csa.ATTN_EINVAL                           # outputs overlap
     assert call(t=m) == csa.ATTN_EINVAL                           # output overlaps the matrix
 
 
 def test_table_workspace_bytes(L):
-    assert L.attn_table_workspace_bytes(4, 8) == 4 * 8 * 4
+    assert L.attn_table_workspace_bytes(4, 8) == 16            # one bit per cell, whole 16 B
+    assert L.attn_table_workspace_bytes(1000, 64) == (1000 * 64 // 32) * 4
     assert L.attn_table_workspace_bytes(0, 8) == 0
     assert L.attn_table_workspace_bytes(1 << 30, 1 << 20) == 0
 

@@ -66,19 +66,23 @@ def test_matrix_to_table(dtype, T, D):
     assert np.array_equal(_bits(x, dtype), wx)
 
 
+@pytest.mark.parametrize("order", ["shuffled", "ordered"])
 @pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
 @pytest.mark.parametrize("T,D,holes", [(1, 1, 0), (3, 64, 0), (257, 65, 0), (64, 64, 37),
                                        (9, 7, 5)])
-def test_table_to_matrix(dtype, T, D, holes):
-    """Rows in a shuffled order, some cells left out: the pivot equals the
-    oracle's bit for bit (oracle on the raw bit patterns, holes = NaN bits)."""
+def test_table_to_matrix(dtype, T, D, holes, order):
+    """Rows shuffled, or in (t, d) order (whole waves of consecutive cells),
+    some cells left out: the pivot equals the oracle's bit for bit (oracle on
+    the row numbers, holes = NaN bits)."""
     import causal_softmax_attention_amd as csa
     m = _values(40 + T + D, T, D, dtype)
     t, d, x = tables.table(m.view(NP_BITS[dtype]))
     rng = np.random.default_rng(T * 100 + D)
     keep = rng.permutation(t.size)[: t.size - holes]
+    if order == "ordered":
+        keep = np.sort(keep)
     t, d, x = t[keep], d[keep], x[keep]
-    note(f"table_to_matrix {dtype} {T}x{D} holes={holes}")
+    note(f"table_to_matrix {dtype} {T}x{D} holes={holes} {order}")
     got = csa.attn_table_to_matrix(torch.from_numpy(t).to(DEV), torch.from_numpy(d).to(DEV),
                                    _to_dev(x, dtype), T, D)
     torch.cuda.synchronize()
@@ -118,6 +122,31 @@ def test_table_to_matrix_status(case, code):
                                           T, D, status=status, check=False)
     torch.cuda.synchronize()
     assert int(status2.item()) == 0
+
+
+@pytest.mark.parametrize("where", ["run", "lane"])
+def test_duplicate_in_ordered_rows(where):
+    """An ordered table with one 64-row stretch sent twice: whole waves of
+    consecutive cells see it through the run's word masks ("run": the repeat
+    starts on a wave boundary), other waves through their lanes' bits."""
+    import causal_softmax_attention_amd as csa
+    T, D = 8, 64
+    t, d, x = tables.table(np.arange(T * D, dtype=np.float32).reshape(T, D))
+    start = 64 if where == "run" else 70
+    t2 = np.concatenate([t, t[start:start + 64]])
+    d2 = np.concatenate([d, d[start:start + 64]])
+    x2 = np.concatenate([x, x[start:start + 64]])
+    with pytest.raises(ValueError):
+        tables.matrix(t2, d2, x2, T, D)
+    note(f"duplicate in ordered rows ({where})")
+    _, status = csa.attn_table_to_matrix(*(torch.from_numpy(a).to(DEV) for a in (t2, d2, x2)),
+                                         T, D, check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 2
+    # the table without the repeat is clean and exact
+    got = csa.attn_table_to_matrix(*(torch.from_numpy(a).to(DEV) for a in (t, d, x)), T, D)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy(), tables.matrix(t, d, x, T, D))
 
 
 def test_table_workload_round_trip():
