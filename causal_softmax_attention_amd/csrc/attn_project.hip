@@ -13,14 +13,15 @@
 // one head x all three matrices; wave w forms matrix w / 4 for 64 of the
 // tokens.  A wave accumulates the transposed tiles C^T = W^T X^T
 // (v_mfma_f32_32x32x16_bf16, float32 accumulators), so a lane holds one token
-// and 16 of its features and stores them as 8-byte runs of one output row.  K-chunks of 64 stream through two
-// LDS stages filled by asynchronous bounds-checked buffer loads (rows past the
-// last token read as zeros): the 256 x 64 slice of x and the 64 x 64 block of
-// each weight matrix.  The W^T operand comes from transposing LDS reads
+// and 16 of its features and stores them as 8-byte runs of one output row.
+// K-chunks of 64 stream through two LDS stages filled by asynchronous
+// bounds-checked buffer loads (rows past the last token read as zeros): the
+// 256 x 64 slice of x and the 64 x 64 block of each weight matrix.  The W^T operand comes from transposing LDS reads
 // (ds_read_b64_tr_b16: lane i gets column i, rows 4h..4h+3 and 8+4h..8+4h+3 of
 // a 16-row chunk); the x operand is read with the same row order, two 8-byte
-// reads per lane.  Workgroups of one 256-token block run on one XCD, head by
-// head, so that block of x is read from HBM once and reused from that XCD's L2.
+// reads per lane.  Workgroups of one XCD run in tiles of 4 token blocks x 8
+// heads (the 32 it holds at once), so each tile reads its blocks of x and its
+// heads' weights from HBM once and reuses them from that XCD's L2.
 //
 // Every other case (float32, float64, or a Dm that is not a multiple of 64):
 // a tiled VALU kernel, 64 tokens x one head per workgroup, each thread 4
@@ -75,11 +76,17 @@ __global__ __launch_bounds__(kThreads, 1) void project_bf16_mfma(
     const __bf16* __restrict__ w2, __bf16* __restrict__ o0, __bf16* __restrict__ o1,
     __bf16* __restrict__ o2, int M, int N, int Dm, int H, int nrt) {
   __shared__ ProjStage st0, st1;
-  // workgroup b runs on XCD b % 8: the blocks of one XCD are token blocks
-  // xcd, xcd + 8, ..., each for every head in turn
+  // workgroup b runs on XCD b % 8 and takes token block xcd + 8 k.  The XCD's
+  // workgroups go in tiles of RB token blocks x HB heads (32 at most, as many
+  // as the XCD runs at once), so a tile reads RB blocks of x and HB heads of
+  // weights, each from HBM once and then from the XCD's L2
+  const int HB = H < 8 ? H : 8, RB = 32 / HB, BS = HB * RB;
+  const int hgroups = (H + HB - 1) / HB;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int rt = (slot / H) * 8 + xcd, head = slot % H;
-  if (rt >= nrt) return;
+  const int blk = slot / BS, idx = slot - blk * BS;
+  const int rtg = blk / hgroups, hgi = blk - rtg * hgroups;
+  const int rt = (rtg * RB + idx / HB) * 8 + xcd, head = hgi * HB + idx % HB;
+  if (rt >= nrt || head >= H) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mat = wave >> 2, tg = wave & 3;
@@ -245,7 +252,9 @@ hipError_t launch_project(int elem_bytes, int64_t B, int64_t N, int64_t Dm, int6
   if (hipError_t e = mark(tm.start[kTimerProject], stream)) return e;
   if (project_uses_mfma(elem_bytes, M, Dm, H)) {
     const int nrt = (int)((M + kTok - 1) / kTok);
-    const unsigned grid = (unsigned)(8 * ((nrt + 7) / 8) * H);
+    const int64_t HB = H < 8 ? H : 8, RB = 32 / HB, hgroups = (H + HB - 1) / HB;
+    const int64_t per_xcd = (nrt + 7) / 8;   // token blocks of one XCD
+    const unsigned grid = (unsigned)(8 * ((per_xcd + RB - 1) / RB) * hgroups * (HB * RB));
     hipLaunchKernelGGL(project_bf16_mfma, dim3(grid), dim3(kThreads), 0, stream,
                        (const __bf16*)x, (const __bf16*)wq, (const __bf16*)wk, (const __bf16*)wv,
                        (__bf16*)q, (__bf16*)k, (__bf16*)v, (int)M, (int)N, (int)Dm, (int)H, nrt);
