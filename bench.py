@@ -5,7 +5,7 @@ loss sum(o^2)/2) over the bfloat16 workload of 8 x 32 heads x 4096 tokens,
 D = 64, inputs resident in HBM before the timed region.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
-                    [--no-secondary]
+                    [--no-secondary] [--steps-before-only] [--copy-calibration]
 
 value: algorithmic TFLOP/s of the whole step.  Algorithmic work counts only the
 N(N+1)/2 pairs (i, j <= i) of each head: 4 D flops per pair in the forward
@@ -341,6 +341,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--steps-before-only", action="store_true",
+                    help="time only the Q/K/V projection and the long-table adapter (one JSON "
+                         "line of those); for profiling their kernels")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy (3x), the known-size reference "
                          "for rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -364,6 +367,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.steps_before_only:
+        print(json.dumps({"steps_before_the_path": steps_before_the_path(args.steps)}))
+        return
     log("generating bf16_4k inputs")
     a, (q, k, v), _ = make_inputs("bf16_4k")
     B, H, N = q.shape[:3]
