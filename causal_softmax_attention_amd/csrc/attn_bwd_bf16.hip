@@ -16,19 +16,23 @@
 // per channel-clock on this part, far too slow for a dQ accumulated across key
 // blocks):
 //   1. prep: -delta_i and -lse_i / scale per row (one pass over O and dO),
-//   2. dK/dV, key-stationary: a wave owns 64 keys whose K and V stay in
+//   2. dK/dV, key-stationary: a wave owns 32 keys whose K and V stay in
 //      registers as MFMA B operands; 128-query stages (Q, dO, and the two
 //      per-row values) stream through a 3-stage LDS ring filled by
 //      asynchronous buffer loads.  S = Q K^T and dP = dO V^T are formed as
 //      query x key accumulators, so after rounding to bf16 they are the B
 //      operands of dV^T = dO^T P and dK^T = Q^T dS, whose A operands come from
 //      transposing LDS reads of the same Q / dO rows.
-//   3. dQ, query-stationary: a wave owns 64 queries (Q, dO in registers, its
+//   3. dQ, query-stationary: a wave owns 32 queries (Q, dO in registers, its
 //      two per-row values per lane); key tiles (K, V) stream through LDS.  S^T
 //      and dP^T are key x query accumulators, so dS^T is the B operand of
 //      dQ^T = K^T dS^T.
-// Each wave holds one SIMD (up to 512 registers) and issues its MFMAs among
-// independent exp / VALU work.
+// A workgroup is 8 waves (256 stationary rows), two waves per SIMD, each within
+// 256 VGPRs: every accumulator then stays in the VGPRs that the exp / VALU work
+// reads, with no AGPR copies, and each SIMD's two waves overlap one another's
+// MFMA and VALU phases.  (With 64 rows per wave and one wave per SIMD the
+// working set passed 256 VGPRs, and the compiler moved about two accumulator
+// registers between AGPRs and VGPRs per MFMA.)
 #include "common.h"
 #include "launch.h"
 #include "mfma_bf16.h"
@@ -40,9 +44,10 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsW = 64;               // stationary rows per wave
+constexpr int kKT = 1;                   // 32-row MFMA columns of stationary rows per wave
+constexpr int kRowsW = 32 * kKT;         // stationary rows per wave
 constexpr int kBlk = kRowsW * kWaves;    // stationary rows per workgroup
 constexpr int kT = 64;                   // streamed rows per tile
 constexpr int kT2 = 2 * kT;              // streamed rows per LDS stage (two tiles per barrier)
@@ -78,7 +83,7 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
 
 // ---- dK / dV, key-stationary -------------------------------------------------
 //
-// A wave owns 64 keys (K, V rows in registers as MFMA B operands) and walks the
+// A wave owns 32 keys (K, V rows in registers as MFMA B operands) and walks the
 // queries in 32-query halves.  Per half n:
 //   A(n): S' = Q K^T - lse/scale and dP' = dO V^T - delta (query rows x key
 //         columns), the accumulators starting from -lse/scale and -delta of
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
 // halves 4s..4s+3; step j of stage s reads half 4s+j+1 (for j = 3 that is the
 // next stage) and half 4s+j-1 (for j = 0 the previous one), so one barrier
 // per stage, after step 0, both publishes stage s+1 and frees the previous
-// stage's buffer for stage s+2.  All four waves of a workgroup walk the same
+// stage's buffer for stage s+2.  All eight waves of a workgroup walk the same
 // halves from the workgroup's first key; halves before a wave's diagonal are
 // fully masked (weight 0), so they add nothing.
 struct alignas(16) QStage {
@@ -107,15 +112,15 @@ struct alignas(16) QStage {
 };
 
 struct DkdvPipe {
-  floatx16 s[2], dp[2];          // A(n) results, consumed by B(n)
-  uint32_t pp[2][8], dsp[2][8];  // B(n-1) results, consumed by C(n-1)
+  floatx16 s[kKT], dp[kKT];          // A(n) results, consumed by B(n)
+  uint32_t pp[kKT][8], dsp[kKT][8];  // B(n-1) results, consumed by C(n-1)
 };
 
 // A: S' and dP' of the 32 queries at rows row0.. of a stage.
 __device__ __forceinline__ void dkdv_scores(const QStage& st, int row0, int lane,
-                                            const bf16x8_t (&kop)[2][4],
-                                            const bf16x8_t (&vop)[2][4], floatx16 (&s)[2],
-                                            floatx16 (&dp)[2]) {
+                                            const bf16x8_t (&kop)[kKT][4],
+                                            const bf16x8_t (&vop)[kKT][4], floatx16 (&s)[kKT],
+                                            floatx16 (&dp)[kKT]) {
   const int i32 = lane & 31, h = lane >> 5;
   bf16x8_t qa[4], oa[4];
 #pragma unroll
@@ -132,7 +137,7 @@ __device__ __forceinline__ void dkdv_scores(const QStage& st, int row0, int lane
     ds[4 * g + 0] = b.x; ds[4 * g + 1] = b.y; ds[4 * g + 2] = b.z; ds[4 * g + 3] = b.w;
   }
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < kKT; ++kt) {
     floatx16 a = ls, b = ds;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -149,13 +154,13 @@ __device__ __forceinline__ void dkdv_scores(const QStage& st, int row0, int lane
 // (a select).  Queries past the end need no mask: their Q and dO rows read as
 // zeros, so their dS is 0 and their P multiplies a zero dO row.
 template <bool MASKED>
-__device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[2], const floatx16 (&dp)[2],
-                                             uint32_t (&pp)[2][8], uint32_t (&dsp)[2][8],
+__device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[kKT], const floatx16 (&dp)[kKT],
+                                             uint32_t (&pp)[kKT][8], uint32_t (&dsp)[kKT][8],
                                              int qrow0, int kw, int lane, float c_scale,
                                              int causal, int band) {
   const int i32 = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < kKT; ++kt) {
     const int key = kw + 32 * kt + i32;
 #pragma unroll
     for (int pr = 0; pr < 8; ++pr) {
@@ -179,9 +184,9 @@ __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[2], const float
 
 // C: dV^T += dO^T P and dK^T += Q^T dS over the 32 queries at rows row0.. of a stage.
 __device__ __forceinline__ void dkdv_accum(const QStage& st, int row0, int lane,
-                                           const uint32_t (&pp)[2][8],
-                                           const uint32_t (&dsp)[2][8],
-                                           floatx16 (&dkacc)[2][2], floatx16 (&dvacc)[2][2]) {
+                                           const uint32_t (&pp)[kKT][8],
+                                           const uint32_t (&dsp)[kKT][8],
+                                           floatx16 (&dkacc)[2][kKT], floatx16 (&dvacc)[2][kKT]) {
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -189,7 +194,7 @@ __device__ __forceinline__ void dkdv_accum(const QStage& st, int row0, int lane,
       const bf16x8_t otr = read_tr(st.dout, lane, row0 / 16 + half, 32 * dt);
       const bf16x8_t qtr = read_tr(st.q, lane, row0 / 16 + half, 32 * dt);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < kKT; ++kt) {
         dvacc[dt][kt] = mma(otr, chunk_op(pp[kt], half), dvacc[dt][kt]);
         dkacc[dt][kt] = mma(qtr, chunk_op(dsp[kt], half), dkacc[dt][kt]);
       }
@@ -201,15 +206,15 @@ __device__ __forceinline__ void dkdv_accum(const QStage& st, int row0, int lane,
 template <bool MASKED, bool SKIP_C>
 __device__ __forceinline__ void dkdv_step(const QStage& sa, int ra, const QStage& sc, int rc,
                                           int qrow0, int kw, int lane, float c_scale, int causal,
-                                          int band, const bf16x8_t (&kop)[2][4],
-                                          const bf16x8_t (&vop)[2][4], DkdvPipe& pipe,
-                                          floatx16 (&dkacc)[2][2], floatx16 (&dvacc)[2][2]) {
-  uint32_t pp[2][8], dsp[2][8];
+                                          int band, const bf16x8_t (&kop)[kKT][4],
+                                          const bf16x8_t (&vop)[kKT][4], DkdvPipe& pipe,
+                                          floatx16 (&dkacc)[2][kKT], floatx16 (&dvacc)[2][kKT]) {
+  uint32_t pp[kKT][8], dsp[kKT][8];
   if (!SKIP_C) dkdv_accum(sc, rc, lane, pipe.pp, pipe.dsp, dkacc, dvacc);
   dkdv_softmax<MASKED>(pipe.s, pipe.dp, pp, dsp, qrow0, kw, lane, c_scale, causal, band);
   dkdv_scores(sa, ra, lane, kop, vop, pipe.s, pipe.dp);
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       pipe.pp[kt][i] = pp[kt][i];
@@ -221,7 +226,7 @@ __device__ __forceinline__ void dkdv_step(const QStage& sa, int ra, const QStage
 // BANDED: a window of band keys; every stage then takes the masked body.
 // Without it the predicate is causal (causal = 1) or absent (causal = 0).
 template <bool BANDED>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ nlseg,
     const float* __restrict__ ndeltag, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
@@ -238,9 +243,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
   const int kw = kb * kBlk + wave * kRowsW;  // first key of this wave
 
   // stationary B operands: lane holds X[key kw + 32 kt + i32][16 kk + 8 h .. +7]
-  bf16x8_t kop[2][4], vop[2][4];
+  bf16x8_t kop[kKT][4], vop[kKT][4];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < kKT; ++kt) {
     const int key = kw + 32 * kt + i32;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -253,11 +258,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
       vop[kt][kk] = __builtin_bit_cast(bf16x8_t, b);
     }
   }
-  floatx16 dkacc[2][2], dvacc[2][2];  // [dt][kt]: (feature x key) tiles, lane holds a key column
+  floatx16 dkacc[2][kKT], dvacc[2][kKT];  // [dt][kt]: (feature x key) tiles, lane holds a key column
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
+    for (int b = 0; b < kKT; ++b) {
       dkacc[a][b] = floatx16{};
       dvacc[a][b] = floatx16{};
     }
@@ -273,9 +278,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
   auto issue = [&](QStage& s, int t) {
     const int r0 = qstart + t * kT2;
     if (wave < 2) rows_async(rl, s.nlse + 64 * wave, r0 + 64 * wave, lane);
-    else rows_async(rd, s.ndelta + 64 * (wave - 2), r0 + 64 * (wave - 2), lane);
-    tile_async<kT2>(rq, s.q, r0, wave, lane);
-    tile_async<kT2>(ro, s.dout, r0, wave, lane);
+    else if (wave < 4) rows_async(rd, s.ndelta + 64 * (wave - 2), r0 + 64 * (wave - 2), lane);
+    tile_async<kT2, kWaves>(rq, s.q, r0, wave, lane);
+    tile_async<kT2, kWaves>(ro, s.dout, r0, wave, lane);
   };
   DkdvPipe pipe;
   // stage s: cur holds it, nxt stage s + 1, prv stage s - 1 (and receives s + 2)
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16(
 
   // epilogue: lane holds key column kw + 32 kt + i32, feature rows 32 dt + acc_row(r, h)
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < kKT; ++kt) {
     const int key = kw + 32 * kt + i32;
     if (key >= N) continue;
 #pragma unroll

@@ -1,5 +1,5 @@
 // dQ of the bfloat16 causal attention backward on gfx950 MFMA: the
-// query-stationary pass (a wave owns 64 queries; K, V stream through LDS).
+// query-stationary pass (a wave owns 32 queries; K, V stream through LDS).
 // The per-row values it reads, -delta_i and -lse_i / scale, come from the
 // backward's prep kernel (attn_bwd_bf16.hip), which also documents the
 // gradient formulas (pages: "Show HN: automatic deduction of FlashAttention
@@ -13,16 +13,17 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsW = 64;               // queries per wave
+constexpr int kQT = 1;                   // 32-query MFMA columns per wave
+constexpr int kRowsW = 32 * kQT;         // queries per wave
 constexpr int kBlk = kRowsW * kWaves;    // queries per workgroup
 constexpr int kT = 64;                   // keys per tile
 constexpr int kT2 = 2 * kT;              // keys per LDS stage (two tiles per barrier)
 
 // ---- dQ, query-stationary ---------------------------------------------------
 //
-// One key tile of the dQ pass for one wave (64 queries x 64 keys), as two
+// One key tile of the dQ pass for one wave (32 queries x 64 keys), as two
 // halves of 32 keys: the second half's S^T / dP^T MFMAs are issued before the
 // first half's exp / VALU work, and the first half's dQ MFMAs before the
 // second half's, so each wave always has independent MFMA and VALU work in
@@ -31,12 +32,12 @@ constexpr int kT2 = 2 * kT;              // keys per LDS stage (two tiles per ba
 // pairs (past the wave's diagonal or a window's start, or past the end of the
 // sequence), which get weight 0 (a select, not a branch).
 template <bool MASKED>
-__device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[2], const floatx16 (&dp)[2],
-                                                uint32_t (&dsp)[2][8], int kt, int k0, int qw,
+__device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[kQT], const floatx16 (&dp)[kQT],
+                                                uint32_t (&dsp)[kQT][8], int kt, int k0, int qw,
                                                 int N, int i32, int h, float c_scale, int causal,
                                                 int band) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     const int qi = qw + 32 * qt + i32;
 #pragma unroll
     for (int pr = 0; pr < 8; ++pr) {
@@ -57,10 +58,10 @@ __device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[2], const fl
 }
 
 __device__ __forceinline__ void dq_half_scores(const __bf16* ks, const __bf16* vs, int kt,
-                                               int i32, int h, const bf16x8_t (&qop)[2][4],
-                                               const bf16x8_t (&oop)[2][4],
-                                               const float (&nls)[2], const float (&ndl)[2],
-                                               floatx16 (&s)[2], floatx16 (&dp)[2]) {
+                                               int i32, int h, const bf16x8_t (&qop)[kQT][4],
+                                               const bf16x8_t (&oop)[kQT][4],
+                                               const float (&nls)[kQT], const float (&ndl)[kQT],
+                                               floatx16 (&s)[kQT], floatx16 (&dp)[kQT]) {
   bf16x8_t ka[4], va[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
@@ -68,7 +69,7 @@ __device__ __forceinline__ void dq_half_scores(const __bf16* ks, const __bf16* v
     va[kk] = read_row8(vs, 32 * kt + i32, 16 * kk + 8 * h);
   }
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     floatx16 a, b;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -88,12 +89,12 @@ __device__ __forceinline__ void dq_half_scores(const __bf16* ks, const __bf16* v
 template <bool MASKED>
 __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int lane, int k0,
                                         int qw, int N, float c_scale,
-                                        const bf16x8_t (&qop)[2][4], const bf16x8_t (&oop)[2][4],
-                                        const float (&nls)[2], const float (&ndl)[2],
-                                        floatx16 (&dqacc)[2][2], int causal, int band) {
+                                        const bf16x8_t (&qop)[kQT][4], const bf16x8_t (&oop)[kQT][4],
+                                        const float (&nls)[kQT], const float (&ndl)[kQT],
+                                        floatx16 (&dqacc)[2][kQT], int causal, int band) {
   const int i32 = lane & 31, h = lane >> 5;
-  floatx16 s0[2], dp0[2], s1[2], dp1[2];
-  uint32_t dsp0[2][8], dsp1[2][8];
+  floatx16 s0[kQT], dp0[kQT], s1[kQT], dp1[kQT];
+  uint32_t dsp0[kQT][8], dsp1[kQT][8];
   bf16x8_t ktr0[2][2], ktr1[2][2];
   dq_half_scores(ks, vs, 0, i32, h, qop, oop, nls, ndl, s0, dp0);
 #pragma unroll
@@ -111,7 +112,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < kQT; ++qt)
         dqacc[dt][qt] = mma(ktr0[half][dt], chunk_op(dsp0[qt], half), dqacc[dt][qt]);
   dq_half_softmax<MASKED>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale, causal, band);
 #pragma unroll
@@ -119,7 +120,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
+      for (int qt = 0; qt < kQT; ++qt)
         dqacc[dt][qt] = mma(ktr1[half][dt], chunk_op(dsp1[qt], half), dqacc[dt][qt]);
 }
 
@@ -130,7 +131,7 @@ struct alignas(16) KVStage {
 
 // CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does.
 template <bool CAUSAL, bool BANDED>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ nlseg,
     const float* __restrict__ ndeltag, __bf16* __restrict__ dq, int heads, int N, int nqb,
@@ -148,10 +149,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
   const int wq_last = min(qw + kRowsW, N) - 1;
 
   // stationary B operands of S^T = K Q^T and dP^T = V dO^T; per-lane -lse/scale, -delta
-  bf16x8_t qop[2][4], oop[2][4];
-  float nls[2], ndl[2];
+  bf16x8_t qop[kQT][4], oop[kQT][4];
+  float nls[kQT], ndl[kQT];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     const int qi = qw + 32 * qt + i32;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -166,11 +167,11 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
     nls[qt] = qi < N ? nlseg[(size_t)head * N + qi] : 0.f;
     ndl[qt] = qi < N ? ndeltag[(size_t)head * N + qi] : 0.f;
   }
-  floatx16 dqacc[2][2];  // [dt][qt]: (feature x query), lane holds a query column
+  floatx16 dqacc[2][kQT];  // [dt][qt]: (feature x query), lane holds a query column
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) dqacc[a][b] = floatx16{};
+    for (int b = 0; b < kQT; ++b) dqacc[a][b] = floatx16{};
 
   // keys of the workgroup's queries: stages t0 .. ntiles-1 of 128 keys
   const int t0 = band ? max(0, qb * kBlk - band + 1) / kT2 : 0;
@@ -180,8 +181,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
   const uint32_t tbytes = (uint32_t)N * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);
   auto issue = [&](KVStage& s, int t) {
-    tile_async<kT2>(rk, s.k, t * kT2, wave, lane);
-    tile_async<kT2>(rv, s.v, t * kT2, wave, lane);
+    tile_async<kT2, kWaves>(rk, s.k, t * kT2, wave, lane);
+    tile_async<kT2, kWaves>(rv, s.v, t * kT2, wave, lane);
   };
   auto step = [&](KVStage& cur, KVStage& ahead, int t) {
     const bool pre = t + 2 < ntiles;
@@ -199,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
                          qop, oop, nls, ndl, dqacc, causal, band);
       }
     }
-    if (pre) wait_vm_barrier<8>();
+    if (pre) wait_vm_barrier<2 * kT2 / (8 * kWaves)>();
     else wait_vm_barrier<0>();
   };
 
@@ -213,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_bf16(
   }
 
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     const int qi = qw + 32 * qt + i32;
     if (qi >= N) continue;
 #pragma unroll

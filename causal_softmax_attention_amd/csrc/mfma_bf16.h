@@ -115,15 +115,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t head_rsrc(const void* base, ui
 }
 
 // Copy rows [row0, row0 + ROWS) (64 bf16 each) of the resource's head into a
-// swizzled LDS tile.  Every thread of a 256-thread workgroup issues ROWS / 32
-// loads; wave w fills the 1 KiB stretches u * 4 + w, lane l slot l of it, and
-// slot p of the tile holds row p / 8, physical chunk p % 8.
-template <int ROWS>
+// swizzled LDS tile.  Every thread of a WAVES-wave workgroup issues
+// ROWS / (8 WAVES) loads; wave w fills the 1 KiB stretches u * WAVES + w, lane
+// l slot l of it, and slot p of the tile holds row p / 8, physical chunk p % 8.
+template <int ROWS, int WAVES = 4>
 __device__ __forceinline__ void tile_async(__amdgpu_buffer_rsrc_t rsrc, __bf16* tile, int row0,
                                            int wave, int lane) {
+  static_assert(ROWS % (8 * WAVES) == 0, "whole stretches per wave");
 #pragma unroll
-  for (int u = 0; u < ROWS / 32; ++u) {
-    const int s = u * 4 + wave;
+  for (int u = 0; u < ROWS / (8 * WAVES); ++u) {
+    const int s = u * WAVES + wave;
     const int p = s * 64 + lane, row = p >> 3;
     const int logical = (p & 7) ^ swz(row);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)(tile + s * 512), 16,
