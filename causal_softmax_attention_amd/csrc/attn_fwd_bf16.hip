@@ -8,12 +8,17 @@
 // keys j <= i, o_i = sum_j exp(s_ij - m_i) v_j / sum_j exp(s_ij - m_i), and
 // lse_i = m_i + ln sum_j exp(s_ij - m_i).
 //
-// Layout of the work (one workgroup = 4 waves = 256 queries of one head):
-//   * Each wave owns 64 queries (two 32-query MFMA columns).  Q stays in
+// Layout of the work (one workgroup = 4 waves = 128 queries of one head):
+//   * Each wave owns 32 queries (one 32-query MFMA column).  Q stays in
 //     registers as the B operand of S^T = K Q^T (v_mfma_f32_32x32x16_bf16), so
 //     every lane holds one query column of the score tile: the softmax state
 //     (reference max m, running sum l) is per lane, no row reduction crosses
 //     lanes except the final l_lane + l_(lane^32).
+//   * Three workgroups share a CU: three waves per SIMD, each within 168
+//     VGPRs, so while one wave waits on its score MFMAs another forms weights.
+//     (Two waves of 64 queries each ran about 10 % slower: at 256 VGPRs the
+//     compiler cannot hoist the V reads, and a third of the latency hiding is
+//     lost.)
 //   * Keys stream in tiles of 64 through a 3-stage LDS ring, filled by
 //     asynchronous bounds-checked buffer loads two tiles ahead (one barrier per
 //     tile).  K rows feed the A operand with plain 16-byte reads; V rows are
@@ -47,7 +52,8 @@ using namespace mfma;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kQW = 64;                 // queries per wave
+constexpr int kQT = 1;                  // 32-query MFMA columns per wave (168 VGPRs hold one)
+constexpr int kQW = 32 * kQT;           // queries per wave
 constexpr int kBr = kQW * kWaves;       // queries per workgroup
 constexpr int kBc = 64;                 // keys per tile
 constexpr float kLn2 = 0.6931471805599453f;
@@ -77,11 +83,11 @@ __device__ __forceinline__ bool all_finite_bf16x8(uint4 w) {
 // Weights of one 64-key tile against the lane's reference max, packed to
 // bf16 pairs in B-operand order; returns the lane's sums of the rounded
 // weights per query column.
-__device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][2], float c_scale,
-                                             const float (&mref)[2], uint32_t (&p)[2][2][8],
-                                             float (&part)[2]) {
+__device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][kQT], float c_scale,
+                                             const float (&mref)[kQT], uint32_t (&p)[kQT][2][8],
+                                             float (&part)[kQT]) {
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     const float nm = -mref[qt];
     float acc = 0.f;
 #pragma unroll
@@ -97,24 +103,24 @@ __device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][2], float c_
   }
 }
 
-// One key tile for one wave (64 queries x 64 keys).  MASKED: the tile crosses
+// One key tile for one wave (32 queries x 64 keys).  MASKED: the tile crosses
 // the wave's diagonal or the end of the sequence.
 template <bool MASKED>
 __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __bf16* pscr,
                                          int lane, int k0, int qw, int N, float c_scale,
-                                         int causal, int band, const bf16x8_t (&qop)[2][4],
-                                         floatx16 (&oacc)[2][2], float (&mref)[2],
-                                         float (&lsum)[2]) {
+                                         int causal, int band, const bf16x8_t (&qop)[kQT][4],
+                                         floatx16 (&oacc)[2][kQT], float (&mref)[kQT],
+                                         float (&lsum)[kQT]) {
   const int i32 = lane & 31, h = lane >> 5;
   // ---- S^T = K Q^T: s[kt][qt] holds keys k0 + 32 kt + acc_row(r, h), query column
-  floatx16 s[2][2];
+  floatx16 s[2][kQT];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     bf16x8_t kop[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) kop[kk] = read_row8(ks, 32 * kt + i32, 16 * kk + 8 * h);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < kQT; ++qt) {
       floatx16 acc = floatx16{};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) acc = mma(kop[kk], qop[qt][kk], acc);
@@ -125,7 +131,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+      for (int qt = 0; qt < kQT; ++qt) {
         const int qi = qw + 32 * qt + i32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -135,12 +141,15 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
       }
   }
   // ---- weights against the reference max, exact max only when needed
-  uint32_t p[2][2][8];
-  float part[2];
+  uint32_t p[kQT][2][8];
+  float part[kQT];
   tile_weights(s, c_scale, mref, p, part);
-  if (__any(!(part[0] <= kTau) || !(part[1] <= kTau))) {
+  bool over = false;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) over |= !(part[qt] <= kTau);
+  if (__any(over)) {
+#pragma unroll
+    for (int qt = 0; qt < kQT; ++qt) {
       float mx = -__builtin_inff();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -160,8 +169,8 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
     }
     tile_weights(s, c_scale, mref, p, part);
   }
-  lsum[0] += part[0];
-  lsum[1] += part[1];
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) lsum[qt] += part[qt];
 
   bool vbad = false;
   if (MASKED) {
@@ -179,48 +188,52 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
       for (int dt = 0; dt < 2; ++dt) {
         const bf16x8_t vop = read_tr(vs, lane, c, 32 * dt);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt)
+        for (int qt = 0; qt < kQT; ++qt)
           oacc[dt][qt] = mma(vop, chunk_op(p[qt][c >> 1], c & 1), oacc[dt][qt]);
       }
   } else {
     // ---- select path: a masked pair never multiplies (V holds inf/NaN).  The
-    // weights of one 32-query column go to the wave's LDS area as [query][key].
+    // weights of one 32-query column and 16 keys go to the wave's LDS area as
+    // [query][key].
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+    for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int pr = 0; pr < 8; ++pr) {
-          const int jj = 32 * kt + acc_row(2 * pr, h);  // keys jj, jj + 1
-          *(uint32_t*)(pscr + i32 * kBc + jj) = p[qt][kt][pr];
+        for (int c16 = 0; c16 < 2; ++c16) {
+#pragma unroll
+          for (int pr = 4 * c16; pr < 4 * c16 + 4; ++pr) {
+            const int jj = acc_row(2 * pr, h) - 16 * c16;  // keys 32 kt + 16 c16 + jj, + 1
+            *(uint32_t*)(pscr + i32 * 16 + jj) = p[qt][kt][pr];
+          }
+          __builtin_amdgcn_wave_barrier();
+          const int qi = qw + 32 * qt + i32;
+          for (int jj = 0; jj < 16; ++jj) {
+            const int j = k0 + 32 * kt + 16 * c16 + jj;
+            const float pj = (float)pscr[i32 * 16 + jj];
+            if (absent(qi, j, N, causal, band)) continue;
+#pragma unroll
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+              for (int r2 = 0; r2 < 16; ++r2)
+                oacc[dt][qt][r2] +=
+                    pj * (float)vs[lds_at(32 * kt + 16 * c16 + jj, 32 * dt + acc_row(r2, h))];
+          }
+          __builtin_amdgcn_wave_barrier();
         }
-      __builtin_amdgcn_wave_barrier();
-      const int qi = qw + 32 * qt + i32;
-      for (int jj = 0; jj < kBc; ++jj) {
-        const int j = k0 + jj;
-        const float pj = (float)pscr[i32 * kBc + jj];
-        if (absent(qi, j, N, causal, band)) continue;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int r2 = 0; r2 < 16; ++r2)
-            oacc[dt][qt][r2] += pj * (float)vs[lds_at(jj, 32 * dt + acc_row(r2, h))];
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
   }
 }
 
 // CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does.
 template <bool CAUSAL, bool BANDED>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale,
     int band_arg, float* __restrict__ ndelta, float* __restrict__ nlse, float inv_scale) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
-  __shared__ __bf16 pscr[kWaves][32 * kBc];
+  __shared__ __bf16 pscr[kWaves][32 * 16];
   int head, qb;
   if (!map_block(blockIdx.x, heads, nqb, true, head, qb)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -235,9 +248,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
 
   // Q operand: lane holds q[qw + 32 qt + i32][16 kk + 8 h .. +7]
-  bf16x8_t qop[2][4];
+  bf16x8_t qop[kQT][4];
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     const int qi = qw + 32 * qt + i32;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -246,22 +259,26 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
       qop[qt][kk] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
-  floatx16 oacc[2][2];  // [dt][qt]: O^T tile, lane holds query column
+  floatx16 oacc[2][kQT];  // [dt][qt]: O^T tile, lane holds query column
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) oacc[a][b] = floatx16{};
+    for (int b = 0; b < kQT; ++b) oacc[a][b] = floatx16{};
   // reference exponents start finite, so a tile whose pairs are all absent for
   // a lane gives it weights exp2(-inf) = 0, and its first present pair takes the
   // exact path (the weight overflows against kRefInit)
-  float mref[2] = {kRefInit, kRefInit};
-  float lsum[2] = {0.f, 0.f};
+  float mref[kQT], lsum[kQT];
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    mref[qt] = kRefInit;
+    lsum[qt] = 0.f;
+  }
 
   const uint32_t tbytes = (uint32_t)N * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);
   auto issue = [&](KVStage& s, int t) {
-    tile_async<kBc>(rk, s.k, t * kBc, wave, lane);
-    tile_async<kBc>(rv, s.v, t * kBc, wave, lane);
+    tile_async<kBc, kWaves>(rk, s.k, t * kBc, wave, lane);
+    tile_async<kBc, kWaves>(rv, s.v, t * kBc, wave, lane);
   };
   auto step = [&](KVStage& cur, KVStage& ahead, int t) {
     const bool pre = t + 2 < ntiles;
@@ -276,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
         fwd_tile<false>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band, qop,
                         oacc, mref, lsum);
     }
-    if (pre) wait_vm_barrier<4>();
+    if (pre) wait_vm_barrier<2 * kBc / (8 * kWaves)>();
     else wait_vm_barrier<0>();
   };
 
@@ -293,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(
   // With ndelta given (the loss sum(o^2)/2, so dO = O), also the backward's
   // per-row values from the stored bf16 row: -delta_i = -|o_i|^2 and -lse_i / scale.
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < kQT; ++qt) {
     const int qi = qw + 32 * qt + i32;
     const float l = lsum[qt] + __shfl_xor(lsum[qt], 32);
     const float inv = 1.0f / l;
