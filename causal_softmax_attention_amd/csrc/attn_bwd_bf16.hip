@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   const int band = BANDED ? band_arg : 0;
   __shared__ QStage st0, st1, st2;
   int head, kb;
-  if (!map_block(blockIdx.x, heads, nkb, false, head, kb)) return;
+  if (!map_block(blockIdx.x, heads, nkb, false, 4, head, kb)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int i32 = lane & 31, h = lane >> 5;

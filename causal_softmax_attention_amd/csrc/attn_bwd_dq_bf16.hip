@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
   const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
   int head, qb;
-  if (!map_block(blockIdx.x, heads, nqb, true, head, qb)) return;
+  if (!map_block(blockIdx.x, heads, nqb, true, 4, head, qb)) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int i32 = lane & 31, h = lane >> 5;

@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
   __shared__ KVStage st0, st1, st2;
   __shared__ __bf16 pscr[kWaves][32 * 16];
   int head, qb;
-  if (!map_block(blockIdx.x, heads, nqb, true, head, qb)) return;
+  if (!map_block(blockIdx.x, heads, nqb, true, 8, head, qb)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i32 = lane & 31, h = lane >> 5;
   const size_t base = (size_t)head * N * kD;

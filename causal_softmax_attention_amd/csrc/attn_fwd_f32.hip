@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
   const int band = BANDED ? band_arg : 0;
   __shared__ Smem sm;
   int head, qb;
-  if (!mfma::map_block(blockIdx.x, heads, nqb, true, head, qb)) return;
+  if (!mfma::map_block(blockIdx.x, heads, nqb, true, 4, head, qb)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i32 = lane & 31, h = lane >> 5;
   const size_t base = (size_t)head * N * kD;

@@ -83,16 +83,24 @@ __device__ __forceinline__ bf16x8_t chunk_op(const uint32_t* packed8, int c) {
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 // Workgroup -> (head, block): workgroup b runs on XCD b % 8, so the blocks of
-// head x, x + 8, ... go to XCD x in turn (their shared K/V or Q/dO rows stay in
-// that XCD's L2); within a head, `last_first` chooses whether the last block or block 0
-// comes first.
-__device__ __forceinline__ bool map_block(int b, int heads, int nblk, bool last_first, int& head,
-                                          int& blk) {
+// head x, x + 8, ... go to XCD x (their shared K/V or Q/dO rows stay in that
+// XCD's L2).  An XCD takes its heads in groups of `group`; within a group the
+// blocks start heaviest first across the group's heads (rank 0 of every head,
+// then rank 1, ...), where rank r is block nblk - 1 - r when `last_first` (the
+// causal forward and dQ, whose last block walks the most keys) and block r
+// otherwise.  Under a causal mask the light blocks then fill the end of the
+// launch instead of one head's heavy block starting last.
+__device__ __forceinline__ bool map_block(int b, int heads, int nblk, bool last_first, int group,
+                                          int& head, int& blk) {
   const int xcd = b & 7, slot = b >> 3;
   const int hx = (heads - xcd + 7) >> 3;  // heads with head % 8 == xcd
   if (slot >= hx * nblk) return false;
-  head = xcd + 8 * (slot / nblk);
-  blk = last_first ? nblk - 1 - slot % nblk : slot % nblk;
+  const int chunk = slot / (group * nblk), within = slot - chunk * group * nblk;
+  const int h0 = chunk * group;
+  const int gc = min(group, hx - h0);     // heads in this group (the last may be short)
+  const int r = within / gc, hi = h0 + within % gc;
+  head = xcd + 8 * hi;
+  blk = last_first ? nblk - 1 - r : r;
   return true;
 }
 
