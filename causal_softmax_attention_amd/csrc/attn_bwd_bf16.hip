@@ -307,8 +307,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   issue(st0, 0);
   if (nst > 1) issue(st1, 1);
   wait_vm_barrier<0>();
-  dkdv_scores(st0, 0, lane, kop, vop, pipe.s, pipe.dp);  // A(0)
-  stage(T{}, T{}, st0, st1, st2, 0);
+  if (causal && kw >= qstart + kT2 && nst > 1) {
+    // no query of stage 0 sees this wave's keys: only the stage's barrier and
+    // loads, A of stage 1's first half, and zero weights for the C of stage
+    // 0's last half (issued by stage 1's first step)
+    wait_vm_barrier<0>();
+    if (2 < nst) issue(st2, 2);
+    dkdv_scores(st1, 0, lane, kop, vop, pipe.s, pipe.dp);
+#pragma unroll
+    for (int kt = 0; kt < kKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pipe.pp[kt][i] = 0u;
+        pipe.dsp[kt][i] = 0u;
+      }
+  } else {
+    dkdv_scores(st0, 0, lane, kop, vop, pipe.s, pipe.dp);  // A(0)
+    stage(T{}, T{}, st0, st1, st2, 0);
+  }
   if (nst > 1) stage(T{}, Fl{}, st1, st2, st0, 1);
   for (int s = 2; s < nst; s += 3) {
     stage(LM{}, Fl{}, st2, st0, st1, s);
