@@ -17,7 +17,7 @@
 // blocks):
 //   1. prep: -delta_i and -lse_i / scale per row (one pass over O and dO),
 //   2. dK/dV, key-stationary: a wave owns 32 keys whose K and V stay in
-//      registers as MFMA B operands; 128-query stages (Q, dO, and the two
+//      registers as MFMA B operands; 64-query stages (Q, dO, and the two
 //      per-row values) stream through a 3-stage LDS ring filled by
 //      asynchronous buffer loads.  S = Q K^T and dP = dO V^T are formed as
 //      query x key accumulators, so after rounding to bf16 they are the B
@@ -27,8 +27,9 @@
 //      two per-row values per lane); key tiles (K, V) stream through LDS.  S^T
 //      and dP^T are key x query accumulators, so dS^T is the B operand of
 //      dQ^T = K^T dS^T.
-// A workgroup is 8 waves (256 stationary rows), two waves per SIMD, each within
-// 256 VGPRs: every accumulator then stays in the VGPRs that the exp / VALU work
+// A workgroup is 4 waves (128 stationary rows) and two workgroups share a CU:
+// two waves per SIMD, each within 256 VGPRs, from workgroups that do not share
+// barriers.  Every accumulator then stays in the VGPRs that the exp / VALU work
 // reads, with no AGPR copies, and each SIMD's two waves overlap one another's
 // MFMA and VALU phases.  (With 64 rows per wave and one wave per SIMD the
 // working set passed 256 VGPRs, and the compiler moved about two accumulator
@@ -44,13 +45,13 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKT = 1;                   // 32-row MFMA columns of stationary rows per wave
 constexpr int kRowsW = 32 * kKT;         // stationary rows per wave
 constexpr int kBlk = kRowsW * kWaves;    // stationary rows per workgroup
 constexpr int kT = 64;                   // streamed rows per tile
-constexpr int kT2 = 2 * kT;              // streamed rows per LDS stage (two tiles per barrier)
+constexpr int kT2 = kT;                  // streamed rows per LDS stage
 
 // Per row: -delta_i = -sum_d dO_id O_id and -lse_i / scale, the values the
 // score accumulators of both passes start from (so that they end as
@@ -96,14 +97,15 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
 // B(n) and C(n-1) together: the MFMAs of A and C overlap the exp / VALU work of
 // B with no result waited on inside a step.
 //
-// Queries stream through a 3-stage LDS ring of 128-row stages (Q, dO, and
+// Queries stream through a 3-stage LDS ring of 64-row stages (Q, dO, and
 // -lse/scale, -delta), filled by asynchronous buffer loads.  Stage s holds
-// halves 4s..4s+3; step j of stage s reads half 4s+j+1 (for j = 3 that is the
-// next stage) and half 4s+j-1 (for j = 0 the previous one), so one barrier
-// per stage, after step 0, both publishes stage s+1 and frees the previous
-// stage's buffer for stage s+2.  All eight waves of a workgroup walk the same
-// halves from the workgroup's first key; halves before a wave's diagonal are
-// fully masked (weight 0), so they add nothing.
+// halves 2s and 2s+1.  Step 0 of stage s forms A(2s+1) from its own rows
+// 32.. and C(2s-1) from the previous stage's rows 32..; step 1 forms A(2s+2)
+// from the next stage's rows 0.. and C(2s) from its own rows 0...  So one
+// barrier per stage, between the two steps, both publishes stage s+1 and
+// frees the previous stage's buffer for stage s+2.  All four waves of a
+// workgroup walk the same halves from the workgroup's first key; halves before
+// a wave's diagonal are fully masked (weight 0), so they add nothing.
 struct alignas(16) QStage {
   __bf16 q[kT2 * kD];
   __bf16 dout[kT2 * kD];
@@ -271,14 +273,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   // the last key's window end or N
   const int qstart = causal ? kb * kBlk : 0;
   const int qend = band ? min(N, kb * kBlk + kBlk - 1 + band) : N;
-  const int nst = (qend - qstart + kT2 - 1) / kT2;  // stages of 128 queries
+  const int nst = (qend - qstart + kT2 - 1) / kT2;  // stages of 64 queries
   const uint32_t tbytes = (uint32_t)N * kD * 2, rbytes = (uint32_t)N * 4;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + base, tbytes), ro = head_rsrc(dout + base, tbytes);
   const __amdgpu_buffer_rsrc_t rl = head_rsrc(nlseg + rbase, rbytes), rd = head_rsrc(ndeltag + rbase, rbytes);
   auto issue = [&](QStage& s, int t) {
     const int r0 = qstart + t * kT2;
-    if (wave < 2) rows_async(rl, s.nlse + 64 * wave, r0 + 64 * wave, lane);
-    else if (wave < 4) rows_async(rd, s.ndelta + 64 * (wave - 2), r0 + 64 * (wave - 2), lane);
+    if (wave == 0) rows_async(rl, s.nlse, r0, lane);
+    else if (wave == 1) rows_async(rd, s.ndelta, r0, lane);
     tile_async<kT2, kWaves>(rq, s.q, r0, wave, lane);
     tile_async<kT2, kWaves>(ro, s.dout, r0, wave, lane);
   };
@@ -287,19 +289,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   auto stage = [&](auto masked, auto first, QStage& cur, QStage& nxt, QStage& prv, int s) {
     constexpr bool M = decltype(masked)::value, F = decltype(first)::value;
     const int q0 = qstart + s * kT2;
-    dkdv_step<M, F>(cur, 32, prv, 96, q0, kw, lane, c_scale, causal, band, kop, vop, pipe,
+    dkdv_step<M, F>(cur, 32, prv, 32, q0, kw, lane, c_scale, causal, band, kop, vop, pipe,
                     dkacc, dvacc);
     wait_vm_barrier<0>();  // stage s + 1 has landed; every wave is done with prv
     if (s + 2 < nst) issue(prv, s + 2);
-    dkdv_step<M, false>(cur, 64, cur, 0, q0 + 32, kw, lane, c_scale, causal, band, kop, vop,
-                        pipe, dkacc, dvacc);
-    dkdv_step<M, false>(cur, 96, cur, 32, q0 + 64, kw, lane, c_scale, causal, band, kop, vop,
-                        pipe, dkacc, dvacc);
-    dkdv_step<M, false>(nxt, 0, cur, 64, q0 + 96, kw, lane, c_scale, causal, band, kop, vop,
+    dkdv_step<M, false>(nxt, 0, cur, 0, q0 + 32, kw, lane, c_scale, causal, band, kop, vop,
                         pipe, dkacc, dvacc);
   };
   // stages 0 and 1 hold the block's diagonal (masked body); later stages lie
   // wholly after every key of the block, so only a window masks them
+  static_assert(kBlk == 2 * kT2, "the block's diagonal spans stages 0 and 1");
   using LM = std::integral_constant<bool, BANDED>;
   using T = std::true_type;
   using Fl = std::false_type;
@@ -331,11 +330,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
     if (s + 1 < nst) stage(LM{}, Fl{}, st0, st1, st2, s + 1);
     if (s + 2 < nst) stage(LM{}, Fl{}, st1, st2, st0, s + 2);
   }
-  // C of the last half (rows 96.. of the last stage)
+  // C of the last half (rows 32.. of the last stage)
   {
     const int r = (nst - 1) % 3;
     const QStage& last = r == 0 ? st0 : r == 1 ? st1 : st2;
-    dkdv_accum(last, 96, lane, pipe.pp, pipe.dsp, dkacc, dvacc);
+    dkdv_accum(last, 32, lane, pipe.pp, pipe.dsp, dkacc, dvacc);
   }
 
   // epilogue: lane holds key column kw + 32 kt + i32, feature rows 32 dt + acc_row(r, h)

@@ -13,13 +13,13 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kQT = 1;                   // 32-query MFMA columns per wave
 constexpr int kRowsW = 32 * kQT;         // queries per wave
 constexpr int kBlk = kRowsW * kWaves;    // queries per workgroup
 constexpr int kT = 64;                   // keys per tile
-constexpr int kT2 = 2 * kT;              // keys per LDS stage (two tiles per barrier)
+constexpr int kT2 = kT;                  // keys per LDS stage
 
 // ---- dQ, query-stationary ---------------------------------------------------
 //
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
 #pragma unroll
     for (int b = 0; b < kQT; ++b) dqacc[a][b] = floatx16{};
 
-  // keys of the workgroup's queries: stages t0 .. ntiles-1 of 128 keys
+  // keys of the workgroup's queries: stages t0 .. ntiles-1 of kT2 keys
   const int t0 = band ? max(0, qb * kBlk - band + 1) / kT2 : 0;
   const int kend = causal ? min(N, qb * kBlk + kBlk) : N;
   const int ntiles = (kend + kT2 - 1) / kT2;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
     const bool pre = t + 2 < ntiles;
     if (pre) issue(ahead, t + 2);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < kT2 / kT; ++sub) {
       const int k0 = t * kT2 + sub * kT;
       if (k0 <= whi && k0 + kT - 1 >= wlo) {
         // masked: some pair of the tile is absent for some query of the wave
