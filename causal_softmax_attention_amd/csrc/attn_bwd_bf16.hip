@@ -225,7 +225,8 @@ __device__ __forceinline__ void dkdv_step(const QStage& sa, int ra, const QStage
   __builtin_amdgcn_sched_barrier(0);  // keep each step's schedule to itself
 }
 
-// BANDED: a window of band keys; every stage then takes the masked body.
+// BANDED: a window of band keys; stages that reach its far edge take the
+// masked body too.
 // Without it the predicate is causal (causal = 1) or absent (causal = 0).
 template <bool BANDED>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
@@ -297,11 +298,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
                         pipe, dkacc, dvacc);
   };
   // stages 0 and 1 hold the block's diagonal (masked body); later stages lie
-  // wholly after every key of the block, so only a window masks them
+  // wholly after every key of the block, so only a window's far edge masks
+  // them: stage s does once its last query minus the block's first key
+  // reaches band, i.e. from stage edge on.  Stages 2 .. edge - 1 (rounded down
+  // to whole turns of the 3-stage ring) take the plain body, the rest the
+  // masked one.
   static_assert(kBlk == 2 * kT2, "the block's diagonal spans stages 0 and 1");
-  using LM = std::integral_constant<bool, BANDED>;
   using T = std::true_type;
   using Fl = std::false_type;
+  const int edge = BANDED ? (band - kT2 + 1 + kb * kBlk - qstart + kT2 - 1) / kT2 : nst;
+  const int plain_end = BANDED ? 2 + 3 * (max(edge - 2, 0) / 3) : nst;
 
   issue(st0, 0);
   if (nst > 1) issue(st1, 1);
@@ -325,10 +331,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
     stage(T{}, T{}, st0, st1, st2, 0);
   }
   if (nst > 1) stage(T{}, Fl{}, st1, st2, st0, 1);
-  for (int s = 2; s < nst; s += 3) {
-    stage(LM{}, Fl{}, st2, st0, st1, s);
-    if (s + 1 < nst) stage(LM{}, Fl{}, st0, st1, st2, s + 1);
-    if (s + 2 < nst) stage(LM{}, Fl{}, st1, st2, st0, s + 2);
+  int s = 2;
+  for (; s < min(plain_end, nst); s += 3) {
+    stage(Fl{}, Fl{}, st2, st0, st1, s);
+    if (s + 1 < nst) stage(Fl{}, Fl{}, st0, st1, st2, s + 1);
+    if (s + 2 < nst) stage(Fl{}, Fl{}, st1, st2, st0, s + 2);
+  }
+  if (BANDED) {
+    for (; s < nst; s += 3) {
+      stage(T{}, Fl{}, st2, st0, st1, s);
+      if (s + 1 < nst) stage(T{}, Fl{}, st0, st1, st2, s + 1);
+      if (s + 2 < nst) stage(T{}, Fl{}, st1, st2, st0, s + 2);
+    }
   }
   // C of the last half (rows 32.. of the last stage)
   {
