@@ -80,6 +80,22 @@ def test_small_fwd_bwd(dtype, shape):
     _check_bwd(a, grads)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_head_groups(dtype):
+    """21 heads: an XCD's heads (workgroup b runs on XCD b % 8) come in groups
+    of 4 or 8 whose last group is short here (3 and 2 heads per XCD), and
+    each head has several blocks.  Every (head, block) must be computed
+    exactly once: all heads against the oracle."""
+    B, H, N = 3, 7, 300
+    a = inp.attention_inputs(21, B, H, N, dtype)
+    note(f"head groups fwd+bwd {dtype} B={B} H={H} N={N}")
+    q, k, v = (to_dev(getattr(a, x), dtype) for x in "qkv")
+    o, lse = run_fwd(q, k, v, S)
+    _check_fwd(a, o, lse)
+    grads = run_bwd(q, k, v, o, o, lse, S)
+    _check_bwd(a, grads)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_general_dout(dtype):
     """An upstream gradient that is not o (same seeded dout on both sides)."""

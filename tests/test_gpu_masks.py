@@ -18,8 +18,11 @@ from metrics import TOL, assert_close, rel_err  # noqa: E402
 
 S = 0.125
 DTYPES = ["f64", "f32", "bf16"]
-# window 1: each query sees only itself; 5000 > every N here: the causal mask
-MASKS = [("full", 0), ("window", 1), ("window", 37), ("window", 200), ("window", 5000)]
+# window 1: each query sees only itself; 5000 > every N here: the causal mask;
+# 400: a key block's walk has interior stages between its diagonal and the
+# window's far edge (plain body) as well as edge stages (masked body)
+MASKS = [("full", 0), ("window", 1), ("window", 37), ("window", 200), ("window", 400),
+         ("window", 5000)]
 SHAPES = [(1, 1, 1), (1, 2, 65), (2, 1, 300), (1, 1, 777)]
 
 
