@@ -253,9 +253,11 @@ def secondary(steps):
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e) / steps
-    # ALU bound: one wave64 VALU op per 4 cycles per SIMD (16 lanes/clock), 7 per
-    # pair with the exp overlapped: 256 CUs x 4 SIMDs x 16 x 2.4 GHz / 7
-    nw_bound = 256 * 4 * 16 * 2.4e9 / 7 / 1e9
+    # ALU bound: a wave64 VALU op holds its SIMD 4 cycles (16 lanes/clock) and
+    # v_exp_f32 8 (transcendentals at half rate, issued like any VALU op); 7 ops
+    # and 1 exp per pair make 36 cycles per 64 pairs: 256 CUs x 4 SIMDs x 64 x
+    # 2.4 GHz / 36
+    nw_bound = 256 * 4 * 64 * 2.4e9 / (7 * 4 + 8) / 1e9
     out["nw_64k"] = {"ms": ms, "Gpairs/s": 65536.0 ** 2 / ms / 1e6,
                      "alu_bound_Gpairs/s": nw_bound,
                      "frac_of_alu_bound": 65536.0 ** 2 / ms / 1e6 / nw_bound}
