@@ -6,22 +6,21 @@
 // Shapes: x [B, N, Dm] (one embedding row per token), W [Dm, H * 64] with
 // head h in columns 64 h .. 64 h + 63, and Q, K, V written as the attention
 // takes them, [B, H, N, 64] (head-major: the reshape and transpose of x W are
-// folded into the stores).  The three products share one read of x: a single
-// launch forms all three.
+// folded into the stores).  One launch forms all three products.
 //
-// bfloat16 with Dm a multiple of 64: one workgroup = 12 waves = 256 tokens x
-// one head x all three matrices; wave w forms matrix w / 4 for 64 of the
-// tokens.  A wave accumulates the transposed tiles C^T = W^T X^T
-// (v_mfma_f32_32x32x16_bf16, float32 accumulators), so a lane holds one token
-// and 16 of its features and stores them as 8-byte runs of one output row.
-// K-chunks of 64 stream through two LDS stages filled by asynchronous
-// bounds-checked buffer loads (rows past the last token read as zeros): the
-// 256 x 64 slice of x and the 64 x 64 block of each weight matrix.  The W^T operand comes from transposing LDS reads
-// (ds_read_b64_tr_b16: lane i gets column i, rows 4h..4h+3 and 8+4h..8+4h+3 of
-// a 16-row chunk); the x operand is read with the same row order, two 8-byte
-// reads per lane.  Workgroups of one XCD run in tiles of 4 token blocks x 8
-// heads (the 32 it holds at once), so each tile reads its blocks of x and its
-// heads' weights from HBM once and reuses them from that XCD's L2.
+// bfloat16 with Dm a multiple of 64: a GEMM over 256-token x 256-column tiles
+// (4 heads of one matrix), 8 waves, 2 per SIMD.  Wave (wr, wc) accumulates the
+// transposed tiles C^T = W^T X^T of tokens 128 wr .. + 127 and head wc of the
+// tile (v_mfma_f32_32x32x16_bf16, float32 accumulators: 4 token x 2 column
+// tiles, 128 registers), so a lane holds one token and 16 of its features and
+// stores them as 8-byte runs of one output row.  64-wide slices of d_model
+// stream through two LDS stages filled by asynchronous bounds-checked buffer
+// loads (rows past the last token read as zeros).  Both operands are read in
+// natural k order without bank conflicts: W^T by transposing reads
+// (ds_read_b64_tr_b16) of 4 consecutive rows, x by 16-byte row reads.  An
+// XCD's workgroups run in patches of 8 token blocks x 4 column groups, so each
+// k-slice of x and W is read from L2 by several of the workgroups it holds at
+// once.
 //
 // Every other case (float32, float64, or a Dm that is not a multiple of 64):
 // a tiled VALU kernel, 64 tokens x one head per workgroup, each thread 4
@@ -36,15 +35,7 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kWaves = 12;               // 3 matrices x 4 token groups
-constexpr int kThreads = 64 * kWaves;
-constexpr int kTok = 256;                // tokens per workgroup (64 per wave)
 constexpr int kKc = 64;                  // d_model per LDS stage
-
-struct alignas(16) ProjStage {
-  __bf16 x[kTok * kKc];     // 256 tokens x 64 (swizzled rows of 64)
-  __bf16 w[3][kKc * 64];    // per matrix: 64 rows of d_model x the head's 64 columns
-};
 
 // One 1 KiB group s (rows 8s .. 8s + 7) of a swizzled LDS tile of 64-column
 // bf16 rows, from rows row0 + 8s .. of a row-major matrix with a row pitch of
@@ -59,105 +50,132 @@ __device__ __forceinline__ void group_async(__amdgpu_buffer_rsrc_t rsrc, __bf16*
                                            0, 0, 0);
 }
 
-// x operand of the token at `row` of the stage for 16-wide chunk c: d_model
-// 16c + 4h .. +3 and 16c + 8 + 4h .. +3 (the row order of the transposing read).
-__device__ __forceinline__ bf16x8_t read_x(const __bf16* tile, int row, int c, int h) {
-  typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
-  const bf16x4_t lo = *(const bf16x4_t*)(tile + lds_at(row, 16 * c + 4 * h));
-  const bf16x4_t hi = *(const bf16x4_t*)(tile + lds_at(row, 16 * c + 8 + 4 * h));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+// W^T operand in natural k order: lane (h, i) gets column col0 + i, d_model
+// rows 16 c + 8 h .. + 7 of a 64-row block (two transposing reads of 4 rows;
+// each 16-lane group reads 4 consecutive rows x 32 bytes, which the swizzle
+// puts in 32 different banks).  Its partner, the x operand, is then a plain
+// 16-byte read of the token's row at 16 c + 8 h.
+__device__ __forceinline__ bf16x8_t read_tr_nat(const __bf16* tile, int lane, int c, int col0) {
+  const int g16 = lane >> 4, c16 = lane & 15;
+  const int col = col0 + 16 * (g16 & 1) + 4 * (c16 & 3);
+  const int row = 16 * c + 8 * (g16 >> 1) + (c16 >> 2);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + lds_at(row, col)));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(tile + lds_at(row + 4, col)));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Wave w forms matrix w / 4 for tokens 64 (w % 4) .. + 63 of the workgroup's
-// 256; waves 0-7 stage the x slice (32 groups of 1 KiB), waves 8-11 the three
-// weight blocks (24 groups).
-__global__ __launch_bounds__(kThreads, 1) void project_bf16_mfma(
+// ---- 256 x 256 tiles, 4 x 2 MFMA tiles per wave ---------------------------
+//
+// Per 16-wide chunk of d_model a wave reads 4 x and 2 W^T operands for 8
+// MFMAs (768 LDS bytes per MFMA).  Measured on x [8, 4096, 2048] with 32
+// heads: 0.84-0.90 ms.  Earlier forms: 12 waves of 2 x 2 tiles with x read in
+// the accumulator-style k order (two 8-byte reads, 2-way bank conflicts),
+// 0.96-1.10 ms; 4 waves of 4 x 4 tiles (256 accumulators, one wave per SIMD),
+// 0.95 ms.
+constexpr int gWaves = 8;
+constexpr int gThreads = 64 * gWaves;
+constexpr int gTok = 256;
+constexpr int gHeads = 4;
+
+struct alignas(16) GemmStage {
+  __bf16 x[gTok * kKc];          // 256 tokens x 64 (swizzled rows of 64)
+  __bf16 w[gHeads][kKc * 64];    // per head: 64 rows of d_model x its 64 columns
+};
+
+__global__ __launch_bounds__(gThreads, 2) void project_bf16_gemm(
     const __bf16* __restrict__ x, const __bf16* __restrict__ w0, const __bf16* __restrict__ w1,
     const __bf16* __restrict__ w2, __bf16* __restrict__ o0, __bf16* __restrict__ o1,
-    __bf16* __restrict__ o2, int M, int N, int Dm, int H, int nrt) {
-  __shared__ ProjStage st0, st1;
-  // workgroup b runs on XCD b % 8 and takes token block xcd + 8 k.  The XCD's
-  // workgroups go in tiles of RB token blocks x HB heads (32 at most, as many
-  // as the XCD runs at once), so a tile reads RB blocks of x and HB heads of
-  // weights, each from HBM once and then from the XCD's L2
-  const int HB = H < 8 ? H : 8, RB = 32 / HB, BS = HB * RB;
-  const int hgroups = (H + HB - 1) / HB;
+    __bf16* __restrict__ o2, int M, int N, int Dm, int H, int nrt, int ncg) {
+  __shared__ GemmStage st0, st1;
+  // workgroup b runs on XCD b % 8 and takes token blocks xcd + 8 k.  An XCD's
+  // workgroups run in patches of 8 of its token blocks x 4 column
+  // groups (the 32 it holds at once), so each k-slice of x is read by 4
+  // workgroups and each k-slice of W by 8 while both sit in that XCD's L2
+  constexpr int PR = 8, PC = 4;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int blk = slot / BS, idx = slot - blk * BS;
-  const int rtg = blk / hgroups, hgi = blk - rtg * hgroups;
-  const int rt = (rtg * RB + idx / HB) * 8 + xcd, head = hgi * HB + idx % HB;
-  if (rt >= nrt || head >= H) return;
+  const int nrx = (nrt - xcd + 7) >> 3;     // token blocks of this XCD
+  const int nct = 3 * ncg;                  // column groups (all three matrices)
+  const int npc = (nct + PC - 1) / PC;
+  const int patch = slot / (PR * PC), within = slot - patch * (PR * PC);
+  const int rp = patch / npc, cp = patch - rp * npc;
+  const int lr = rp * PR + within / PC, ct = cp * PC + within % PC;
+  if (lr >= nrx || ct >= nct) return;
+  const int rt = lr * 8 + xcd;
+  const int mat = ct / ncg, head0 = (ct % ncg) * gHeads;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int mat = wave >> 2, tg = wave & 3;
+  const int wr = wave >> 2, wc = wave & 3;  // tokens 128 wr .., head head0 + wc
   const int i32 = lane & 31, h = lane >> 5;
-  const int m0 = rt * kTok;
+  const int m0 = rt * gTok;
   const uint32_t xpitch = (uint32_t)Dm * 2, wpitch = (uint32_t)H * 128;
   const __amdgpu_buffer_rsrc_t rx = head_rsrc(x, (uint32_t)M * xpitch);
-  const uint32_t wbytes = (uint32_t)Dm * wpitch;
-  const __amdgpu_buffer_rsrc_t rw[3] = {head_rsrc(w0, wbytes), head_rsrc(w1, wbytes),
-                                        head_rsrc(w2, wbytes)};
-  // waves 8-11 stage the weight blocks: group 4 (u & 1) + (wave - 8) of block
-  // u >> 1 for u = 0..5
-  auto issue = [&](ProjStage& s, int k0) {
-    if (wave < 8) {
+  const __amdgpu_buffer_rsrc_t rw =
+      head_rsrc(mat == 0 ? w0 : mat == 1 ? w1 : w2, (uint32_t)Dm * wpitch);
+  // 32 groups of 1 KiB for x (8 token rows each), 32 for W (8 rows of one
+  // head's block each); wave w issues groups w, w + 8, ...
+  auto issue = [&](GemmStage& s, int k0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        group_async(rx, s.x, m0, xpitch, (uint32_t)k0 * 2, 8 * u + wave, lane);
-    } else {
+    for (int u = 0; u < 32 / gWaves; ++u)
+      group_async(rx, s.x, m0, xpitch, (uint32_t)k0 * 2, wave + gWaves * u, lane);
 #pragma unroll
-      for (int u = 0; u < 6; ++u)
-        group_async(rw[u >> 1], s.w[u >> 1], k0, wpitch, (uint32_t)head * 128,
-                    4 * (u & 1) + (wave - 8), lane);
+    for (int u = 0; u < 32 / gWaves; ++u) {
+      const int g = wave + gWaves * u, hh = g >> 3;
+      group_async(rw, s.w[hh], k0, wpitch, (uint32_t)(head0 + hh) * 128, g & 7, lane);
     }
   };
 
-  floatx16 acc[2][2];  // [feature half nt][token half mt]: C^T tiles
+  floatx16 acc[2][4];  // [column tile nt][token tile mt]
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = floatx16{};
+    for (int b = 0; b < 4; ++b) acc[a][b] = floatx16{};
 
-  auto compute = [&](const ProjStage& s) {
-    const __bf16* wt = s.w[0] + mat * (kKc * 64);
+  auto compute = [&](const GemmStage& s) {
+    // the lane as a value the compiler cannot see through: operand addresses
+    // are formed per stage rather than hoisted for both stages (and held)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int li = ln & 31, lh = ln >> 5;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      bf16x8_t xb[2], wa[2];
+      bf16x8_t xb[4], wa[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) xb[mt] = read_x(s.x, 64 * tg + 32 * mt + i32, c, h);
+      for (int mt = 0; mt < 4; ++mt) xb[mt] = read_row8(s.x, 128 * wr + 32 * mt + li, 16 * c + 8 * lh);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) wa[nt] = read_tr(wt, lane, c, 32 * nt);
+      for (int nt = 0; nt < 2; ++nt) wa[nt] = read_tr_nat(s.w[wc], ln, c, 32 * nt);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = mma(wa[nt], xb[mt], acc[nt][mt]);
+        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = mma(wa[nt], xb[mt], acc[nt][mt]);
     }
   };
 
+  // one loop body for both stages (a stage chosen at run time): an unrolled
+  // pair with an exit between its halves made the compiler move the
+  // accumulator registers between paths
   const int nk = Dm / kKc;
   issue(st0, 0);
   wait_vm_barrier<0>();
-  for (int kc = 0; kc < nk; kc += 2) {
-    if (kc + 1 < nk) issue(st1, (kc + 1) * kKc);
-    compute(st0);
-    wait_vm_barrier<0>();  // stage 1 has landed; every wave is done with stage 0
-    if (kc + 1 >= nk) break;
-    if (kc + 2 < nk) issue(st0, (kc + 2) * kKc);
-    compute(st1);
-    wait_vm_barrier<0>();
+  for (int kc = 0; kc < nk; ++kc) {
+    const bool odd = kc & 1;
+    if (kc + 1 < nk) issue(odd ? st0 : st1, (kc + 1) * kKc);
+    compute(odd ? st1 : st0);
+    wait_vm_barrier<0>();  // the next stage has landed; every wave is done with this one
   }
 
-  // epilogue: lane holds token m0 + 64 tg + 32 mt + i32, features
-  // 32 nt + 8 g + 4 h .. +3 in registers 4 g .. 4 g + 3
+  // epilogue: lane holds token m0 + 128 wr + 32 mt + i32, features 32 nt +
+  // 8 g + 4 h .. +3 of head head0 + wc in registers 4 g .. 4 g + 3
   __bf16* out = mat == 0 ? o0 : mat == 1 ? o1 : o2;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int m = m0 + 64 * tg + 32 * mt + i32;
+  for (int mt = 0; mt < 4; ++mt) {
+    const int m = m0 + 128 * wr + 32 * mt + i32;
     if (m >= M) continue;
     const int b = m / N, n = m - b * N;
+    const int head = head0 + wc;
+    if (head >= H) continue;
     __bf16* row = out + (((size_t)b * H + head) * N + n) * kD;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < 2; ++nt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 v;
@@ -165,6 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) void project_bf16_mfma(
         v.y = pack_bf16(acc[nt][mt][4 * g + 2], acc[nt][mt][4 * g + 3]);
         *(uint2*)(row + 32 * nt + 8 * g + 4 * h) = v;
       }
+    }
   }
 }
 
@@ -251,13 +270,14 @@ hipError_t launch_project(int elem_bytes, int64_t B, int64_t N, int64_t Dm, int6
   const int64_t M = B * N;
   if (hipError_t e = mark(tm.start[kTimerProject], stream)) return e;
   if (project_uses_mfma(elem_bytes, M, Dm, H)) {
-    const int nrt = (int)((M + kTok - 1) / kTok);
-    const int64_t HB = H < 8 ? H : 8, RB = 32 / HB, hgroups = (H + HB - 1) / HB;
-    const int64_t per_xcd = (nrt + 7) / 8;   // token blocks of one XCD
-    const unsigned grid = (unsigned)(8 * ((per_xcd + RB - 1) / RB) * hgroups * (HB * RB));
-    hipLaunchKernelGGL(project_bf16_mfma, dim3(grid), dim3(kThreads), 0, stream,
+    const int nrt = (int)((M + gTok - 1) / gTok);
+    const int ncg = (int)((H + gHeads - 1) / gHeads);
+    const int64_t npr = ((nrt + 7) / 8 + 7) / 8, npc = (3 * ncg + 3) / 4;
+    const unsigned grid = (unsigned)(8 * npr * npc * 32);
+    hipLaunchKernelGGL(project_bf16_gemm, dim3(grid), dim3(gThreads), 0, stream,
                        (const __bf16*)x, (const __bf16*)wq, (const __bf16*)wk, (const __bf16*)wv,
-                       (__bf16*)q, (__bf16*)k, (__bf16*)v, (int)M, (int)N, (int)Dm, (int)H, nrt);
+                       (__bf16*)q, (__bf16*)k, (__bf16*)v, (int)M, (int)N, (int)Dm, (int)H, nrt,
+                       ncg);
   } else {
     const dim3 grid((unsigned)((M + kVT - 1) / kVT), (unsigned)H);
     switch (elem_bytes) {
