@@ -4,7 +4,9 @@
 // A group of 8 lanes owns one query row (forward, dQ) or one key row (dK/dV):
 // lane g of the group holds features 8g .. 8g+7 of that row, partial dot
 // products are summed across the group with three lane exchanges, and the
-// group walks the other side's rows through LDS tiles.  Every pair (i, j) with
+// group walks the other side's rows through LDS tiles.  When heads x rows are
+// few, 8 groups share a row, each walking every 8th row of the other side,
+// and merge their partial states at the end (see Split below).  Every pair (i, j) with
 // j <= i is visited by exactly the group that owns it and an absent pair
 // (j > i) is never touched (pages: "Show HN: automatic deduction of
 // FlashAttention kernel from 25 lines of SQL", the join predicate q.t >= k.t and
@@ -22,8 +24,25 @@ namespace {
 constexpr int kG = 8;                    // lanes per row
 constexpr int kF = kD / kG;              // features per lane
 constexpr int kThr = 256;                // threads per workgroup
-constexpr int kRows = kThr / kG;         // rows per workgroup
 constexpr int kTile = 32;                // rows of the streamed side per LDS tile
+constexpr int kSplit = 8;                // groups per row when the rows alone are few
+constexpr int kFewBlocks = 2 * 256;      // fewer 32-row blocks than this (2 per CU): split
+
+// S groups of 8 lanes share a row: group s walks tile rows s, s + S, ... and
+// the S partial results are merged at the end.  S = 1 (32 rows per workgroup,
+// each tile read by 32 rows) when heads x rows give the part enough
+// workgroups; S = 8 when they do not (the 256-token float64 case: 8
+// workgroups), where the walk's serial latency, a float64 exp per pair, set
+// the time.  Measured: 256 tokens float64 fwd+bwd 443 -> 138 us; 4 heads of
+// 1024 tokens 1846 -> 813 us; 16 heads of 2048 float32 tokens (1024 blocks)
+// were 17 % slower split, so they are not.
+__host__ __device__ constexpr bool split_rows(int64_t heads, int64_t N) {
+  return heads * ((N + 31) / 32) < kFewBlocks;
+}
+template <int S>
+struct Split {
+  static constexpr int kRows = kThr / (kG * S);  // rows per workgroup
+};
 
 // Sum over the 8 lanes of a group (aligned groups: xor partners stay inside).
 template <typename A>
@@ -46,7 +65,7 @@ __device__ __forceinline__ void load_tiles(A (*xs)[kD], A (*ys)[kD], const T* x,
   }
 }
 
-template <typename T>
+template <typename T, int S>
 __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v, T* __restrict__ o,
@@ -54,13 +73,15 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
                                                      acc_t<T> scale, int causal, int band,
                                                      acc_t<T>* __restrict__ delta) {
   using A = acc_t<T>;
+  constexpr int kRows = Split<S>::kRows;
   __shared__ A ks[kTile][kD];
   __shared__ A vs[kTile][kD];
   const int head = blockIdx.x / nqb;
   const int qb = nqb - 1 - (blockIdx.x % nqb);  // longest rows first
   const size_t base = (size_t)head * N * kD;
   const int g = threadIdx.x % kG, f0 = kF * g;
-  const int i = qb * kRows + threadIdx.x / kG;
+  const int grp = threadIdx.x / kG, r = grp / S, sp = grp % S;  // row r of the block, split sp
+  const int i = qb * kRows + r;
   const bool valid = i < N;
   const int jlo = band ? i - band + 1 : 0, jhi = causal ? i : N - 1;  // this row's keys
 
@@ -79,7 +100,7 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
     load_tiles(ks, vs, k, v, base, k0, N);
     __syncthreads();
     const int jn = min(kTile, kend - k0);
-    for (int jj = 0; jj < jn; ++jj) {
+    for (int jj = sp; jj < jn; jj += S) {
       const int j = k0 + jj;
       if (j > jhi) break;  // absent pairs past the row (the whole group leaves together)
       if (j < jlo) continue;
@@ -99,6 +120,37 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
 #pragma unroll
       for (int f = 0; f < kF; ++f) acc[f] += p * vs[jj][f0 + f];
     }
+  }
+  if (S > 1) {
+    // merge the splits' (m, l, acc) against the largest m; the tiles' LDS is
+    // free now (every group has left the walk at the barrier)
+    A* mm = &ks[0][0];                     // [kRows][S]
+    A* ll = mm + kRows * S;                // [kRows][S]
+    A* aa = &vs[0][0];                     // [kRows][S][64]
+    static_assert(2 * (kThr / (kG * S)) * S <= kTile * kD && (kThr / kG) * kD <= kTile * kD,
+                  "merge buffers fit the tiles");
+    __syncthreads();
+    if (g == 0) {
+      mm[r * S + sp] = m;
+      ll[r * S + sp] = l;
+    }
+#pragma unroll
+    for (int f = 0; f < kF; ++f) aa[(r * S + sp) * kD + f0 + f] = acc[f];
+    __syncthreads();
+    if (sp != 0) return;
+    A mx = neg_inf<A>();
+    for (int t = 0; t < S; ++t) mx = mx > mm[r * S + t] ? mx : mm[r * S + t];
+    l = 0;
+#pragma unroll
+    for (int f = 0; f < kF; ++f) acc[f] = 0;
+    for (int t = 0; t < S; ++t) {
+      const A mt = mm[r * S + t];
+      const A w = mt == neg_inf<A>() ? A(0) : exp_acc(mt - mx);  // a split that saw no key adds 0
+      l += ll[r * S + t] * w;
+#pragma unroll
+      for (int f = 0; f < kF; ++f) acc[f] += aa[(r * S + t) * kD + f0 + f] * w;
+    }
+    m = mx;
   }
   if (valid) {
     const A inv = A(1) / l;
@@ -131,13 +183,14 @@ __global__ __launch_bounds__(256) void bwd_delta(const T* __restrict__ o, const 
 }
 
 // dK, dV: one group per key j, queries i >= j streamed through LDS.
-template <typename T>
+template <typename T, int S>
 __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
     const acc_t<T>* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int N, int nkb,
     acc_t<T> scale, int causal, int band) {
   using A = acc_t<T>;
+  constexpr int kRows = Split<S>::kRows;
   __shared__ A qs[kTile][kD];
   __shared__ A dos[kTile][kD];
   __shared__ A ls[kTile], ds_[kTile];
@@ -145,7 +198,8 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
   const int kb = blockIdx.x % nkb;  // low key blocks see the most queries: they come first
   const size_t base = (size_t)head * N * kD;
   const int g = threadIdx.x % kG, f0 = kF * g;
-  const int j = kb * kRows + threadIdx.x / kG;
+  const int grp = threadIdx.x / kG, r = grp / S, sp = grp % S;  // key r of the block, split sp
+  const int j = kb * kRows + r;
   const bool valid = j < N;
   const int ilo = causal ? j : 0, ihi = band ? j + band - 1 : N - 1;  // this key's queries
   A kr[kF], vr[kF], gk[kF], gv[kF];
@@ -168,7 +222,7 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
     }
     __syncthreads();
     const int in = min(kTile, qend - q0);
-    for (int ii = 0; ii < in; ++ii) {
+    for (int ii = sp; ii < in; ii += S) {
       if (q0 + ii < ilo || q0 + ii > ihi) continue;  // pair (i, j) absent
       A s = 0, dp = 0;
 #pragma unroll
@@ -187,6 +241,25 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
       }
     }
   }
+  if (S > 1) {
+    // sum the splits' partial dK, dV (in split order) in the tiles' LDS
+    A* pk = &qs[0][0];                     // [kRows][S][64]
+    A* pv = &dos[0][0];
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < kF; ++f) {
+      pk[(r * S + sp) * kD + f0 + f] = gk[f];
+      pv[(r * S + sp) * kD + f0 + f] = gv[f];
+    }
+    __syncthreads();
+    if (sp != 0) return;
+    for (int t = 1; t < S; ++t)
+#pragma unroll
+      for (int f = 0; f < kF; ++f) {
+        gk[f] += pk[(r * S + t) * kD + f0 + f];
+        gv[f] += pv[(r * S + t) * kD + f0 + f];
+      }
+  }
   if (valid) {
 #pragma unroll
     for (int f = 0; f < kF; ++f) {
@@ -197,20 +270,22 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
 }
 
 // dQ: one group per query i, keys j <= i streamed through LDS.
-template <typename T>
+template <typename T, int S>
 __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
     const acc_t<T>* __restrict__ delta, T* __restrict__ dq, int N, int nqb, acc_t<T> scale,
     int causal, int band) {
   using A = acc_t<T>;
+  constexpr int kRows = Split<S>::kRows;
   __shared__ A ks[kTile][kD];
   __shared__ A vs[kTile][kD];
   const int head = blockIdx.x / nqb;
   const int qb = nqb - 1 - (blockIdx.x % nqb);
   const size_t base = (size_t)head * N * kD;
   const int g = threadIdx.x % kG, f0 = kF * g;
-  const int i = qb * kRows + threadIdx.x / kG;
+  const int grp = threadIdx.x / kG, r = grp / S, sp = grp % S;  // query r of the block, split sp
+  const int i = qb * kRows + r;
   const bool valid = i < N;
   A qr[kF], dor[kF], gq[kF];
 #pragma unroll
@@ -229,7 +304,7 @@ __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
     load_tiles(ks, vs, k, v, base, k0, N);
     __syncthreads();
     const int jn = min(kTile, kend - k0);
-    for (int jj = 0; jj < jn; ++jj) {
+    for (int jj = sp; jj < jn; jj += S) {
       const int j = k0 + jj;
       if (j > jhi) break;
       if (j < jlo) continue;
@@ -247,6 +322,18 @@ __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
       for (int f = 0; f < kF; ++f) gq[f] += dsc * ks[jj][f0 + f];
     }
   }
+  if (S > 1) {
+    // sum the splits' partial dQ (in split order) in the tiles' LDS
+    A* pq = &ks[0][0];                     // [kRows][S][64]
+    __syncthreads();
+#pragma unroll
+    for (int f = 0; f < kF; ++f) pq[(r * S + sp) * kD + f0 + f] = gq[f];
+    __syncthreads();
+    if (sp != 0) return;
+    for (int t = 1; t < S; ++t)
+#pragma unroll
+      for (int f = 0; f < kF; ++f) gq[f] += pq[(r * S + t) * kD + f0 + f];
+  }
   if (valid) {
 #pragma unroll
     for (int f = 0; f < kF; ++f) dq[base + (size_t)i * kD + f0 + f] = narrow<T>(gq[f]);
@@ -260,10 +347,13 @@ hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64
                       int64_t N, double scale, const Mask& mk, void* bwd_ws, hipStream_t stream,
                       const Timers& tm) {
   using A = acc_t<T>;
-  const int nqb = (int)((N + kRows - 1) / kRows);
+  const bool split = split_rows(heads, N);
+  const int per = split ? Split<kSplit>::kRows : Split<1>::kRows;
+  const int nqb = (int)((N + per - 1) / per);
+  auto kern = split ? fwd_rowwise<T, kSplit> : fwd_rowwise<T, 1>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
-  hipLaunchKernelGGL(fwd_rowwise<T>, dim3((unsigned)(heads * nqb)), dim3(kThr), 0, stream, q, k,
-                     v, o, (A*)lse, (int)N, nqb, (A)scale, mk.causal, mk.band, (A*)bwd_ws);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(heads * nqb)), dim3(kThr), 0, stream, q, k, v, o,
+                     (A*)lse, (int)N, nqb, (A)scale, mk.causal, mk.band, (A*)bwd_ws);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }
@@ -287,15 +377,18 @@ hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* d
                        o, dout, delta, rows);
     if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
   }
-  const int nb = (int)((N + kRows - 1) / kRows);
+  const bool split = split_rows(heads, N);
+  const int per = split ? Split<kSplit>::kRows : Split<1>::kRows;
+  const int nb = (int)((N + per - 1) / per);
+  auto kdkdv = split ? bwd_dkdv_rowwise<T, kSplit> : bwd_dkdv_rowwise<T, 1>;
+  auto kdq = split ? bwd_dq_rowwise<T, kSplit> : bwd_dq_rowwise<T, 1>;
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
-  hipLaunchKernelGGL(bwd_dkdv_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q,
-                     k, v, dout, (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale, mk.causal,
-                     mk.band);
+  hipLaunchKernelGGL(kdkdv, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q, k, v, dout,
+                     (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale, mk.causal, mk.band);
   if (hipError_t e = mark(tm.stop[kTimerBwdDkdv], stream)) return e;
   if (hipError_t e = mark(tm.start[kTimerBwdDq], stream)) return e;
-  hipLaunchKernelGGL(bwd_dq_rowwise<T>, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q, k,
-                     v, dout, (const A*)lse, delta, dq, (int)N, nb, (A)scale, mk.causal, mk.band);
+  hipLaunchKernelGGL(kdq, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q, k, v, dout,
+                     (const A*)lse, delta, dq, (int)N, nb, (A)scale, mk.causal, mk.band);
   if (hipError_t e = mark(tm.stop[kTimerBwdDq], stream)) return e;
   return hipGetLastError();
 }

@@ -109,3 +109,27 @@ def test_f64_4096_tokens():
         for name, g, w in zip(("dq", "dk", "dv"), grads,
                               oracle.backward_head(qh[0, h], kh[0, h], vh[0, h], None, S)):
             assert_close(name, to_host(g)[0, h], w, TOL["f64"])
+
+
+@pytest.mark.parametrize("mask,window", [(None, 0), ("window", 200), ("full", 0)], ids=str)
+def test_f64_many_heads_unsplit(mask, window):
+    """float64 with 32 heads of 512 tokens: enough 32-row blocks (512) that the
+    row kernels walk each row with one group (a few heads, or short rows, make
+    them split each row's walk over 8 groups).  Heads 0, 13 and 31 against the
+    oracle in full."""
+    B, H, N = 4, 8, 512
+    a = inp.attention_inputs(127, B, H, N, "f64")
+    note(f"f64 unsplit rows B={B} H={H} N={N} mask={mask} window={window}")
+    q, k, v = (to_dev(getattr(a, x), "f64") for x in "qkv")
+    o, lse = run_fwd(q, k, v, S, mask=mask, window=window)
+    grads = run_bwd(q, k, v, o, o, lse, S, mask=mask, window=window)
+    qh, kh, vh = (a.as_f64(x) for x in "qkv")
+    kw = {} if mask is None else {"mask": mask, "window": window}
+    for bh in (0, 13, 31):
+        b, h = divmod(bh, H)
+        wo, wl = oracle.forward_head(qh[b, h], kh[b, h], vh[b, h], S, **kw)[:2]
+        assert_close(f"o[{b},{h}]", to_host(o)[b, h], wo, TOL["f64"])
+        assert_close(f"lse[{b},{h}]", to_host(lse)[b, h], wl, TOL["f64"])
+        want = oracle.backward_head(qh[b, h], kh[b, h], vh[b, h], None, S, **kw)
+        for name, g, w in zip(("dq", "dk", "dv"), grads, want):
+            assert_close(f"{name}[{b},{h}]", to_host(g)[b, h], w, TOL["f64"])
