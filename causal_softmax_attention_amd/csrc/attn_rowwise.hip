@@ -5,8 +5,8 @@
 // lane g of the group holds features 8g .. 8g+7 of that row, partial dot
 // products are summed across the group with three lane exchanges, and the
 // group walks the other side's rows through LDS tiles.  When heads x rows are
-// few, 8 groups share a row, each walking every 8th row of the other side,
-// and merge their partial states at the end (see Split below).  Every pair (i, j) with
+// few, 8 or 32 groups share a row, each walking every 8th or 32nd row of the
+// other side, and merge their partial states at the end (see Split below).  Every pair (i, j) with
 // j <= i is visited by exactly the group that owns it and an absent pair
 // (j > i) is never touched (pages: "Show HN: automatic deduction of
 // FlashAttention kernel from 25 lines of SQL", the join predicate q.t >= k.t and
@@ -25,19 +25,20 @@ constexpr int kG = 8;                    // lanes per row
 constexpr int kF = kD / kG;              // features per lane
 constexpr int kThr = 256;                // threads per workgroup
 constexpr int kTile = 32;                // rows of the streamed side per LDS tile
-constexpr int kSplit = 8;                // groups per row when the rows alone are few
 constexpr int kFewBlocks = 2 * 256;      // fewer 32-row blocks than this (2 per CU): split
 
 // S groups of 8 lanes share a row: group s walks tile rows s, s + S, ... and
 // the S partial results are merged at the end.  S = 1 (32 rows per workgroup,
 // each tile read by 32 rows) when heads x rows give the part enough
-// workgroups; S = 8 when they do not (the 256-token float64 case: 8
-// workgroups), where the walk's serial latency, a float64 exp per pair, set
-// the time.  Measured: 256 tokens float64 fwd+bwd 443 -> 138 us; 4 heads of
-// 1024 tokens 1846 -> 813 us; 16 heads of 2048 float32 tokens (1024 blocks)
-// were 17 % slower split, so they are not.
-__host__ __device__ constexpr bool split_rows(int64_t heads, int64_t N) {
-  return heads * ((N + 31) / 32) < kFewBlocks;
+// workgroups; otherwise the walk's serial latency (a float64 exp per pair)
+// sets the time and the rows' walks are split: S = 8 below 2 blocks of 32
+// rows per CU, S = 32 (one row per workgroup) below 32 blocks.  Measured,
+// float64 fwd+bwd: one head of 256 tokens 443 us unsplit, 138 us at S = 8,
+// 97 us at S = 32; 4 heads of 1024 tokens 1846 us unsplit, 823 us at S = 8,
+// 1210 us at S = 32.  16 heads of 2048 float32 tokens (1024 blocks) were
+// 17 % slower at S = 8, so they stay unsplit.
+__host__ __device__ constexpr int split_for(int64_t heads, int64_t N) {
+  return heads * ((N + 31) / 32) < 32 ? 32 : heads * ((N + 31) / 32) < kFewBlocks ? 8 : 1;
 }
 template <int S>
 struct Split {
@@ -347,10 +348,10 @@ hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64
                       int64_t N, double scale, const Mask& mk, void* bwd_ws, hipStream_t stream,
                       const Timers& tm) {
   using A = acc_t<T>;
-  const bool split = split_rows(heads, N);
-  const int per = split ? Split<kSplit>::kRows : Split<1>::kRows;
+  const int sp = split_for(heads, N);
+  const int per = kThr / (kG * sp);
   const int nqb = (int)((N + per - 1) / per);
-  auto kern = split ? fwd_rowwise<T, kSplit> : fwd_rowwise<T, 1>;
+  auto kern = sp == 32 ? fwd_rowwise<T, 32> : sp == 8 ? fwd_rowwise<T, 8> : fwd_rowwise<T, 1>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(heads * nqb)), dim3(kThr), 0, stream, q, k, v, o,
                      (A*)lse, (int)N, nqb, (A)scale, mk.causal, mk.band, (A*)bwd_ws);
@@ -377,11 +378,12 @@ hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* d
                        o, dout, delta, rows);
     if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
   }
-  const bool split = split_rows(heads, N);
-  const int per = split ? Split<kSplit>::kRows : Split<1>::kRows;
+  const int sp = split_for(heads, N);
+  const int per = kThr / (kG * sp);
   const int nb = (int)((N + per - 1) / per);
-  auto kdkdv = split ? bwd_dkdv_rowwise<T, kSplit> : bwd_dkdv_rowwise<T, 1>;
-  auto kdq = split ? bwd_dq_rowwise<T, kSplit> : bwd_dq_rowwise<T, 1>;
+  auto kdkdv = sp == 32 ? bwd_dkdv_rowwise<T, 32>
+               : sp == 8 ? bwd_dkdv_rowwise<T, 8> : bwd_dkdv_rowwise<T, 1>;
+  auto kdq = sp == 32 ? bwd_dq_rowwise<T, 32> : sp == 8 ? bwd_dq_rowwise<T, 8> : bwd_dq_rowwise<T, 1>;
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
   hipLaunchKernelGGL(kdkdv, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q, k, v, dout,
                      (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale, mk.causal, mk.band);
