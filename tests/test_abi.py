@@ -275,3 +275,14 @@ def test_qkv_project_rejects(L):
     assert call(ptrs=(x, wq, wk, wv, x, k, v)) == csa.ATTN_EINVAL   # q aliases x
     assert call(ptrs=(x, wq, wk, wv, q, q, v)) == csa.ATTN_EINVAL   # k overlaps q
     assert "overlap" in csa.attn_last_error()
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """With no built library every entry point raises (there is no fallback
+    path): the binding's loader names the missing file."""
+    monkeypatch.setattr(csa, "LIB_PATH", str(tmp_path / "libattn.so"))
+    monkeypatch.setattr(csa, "_LIB", None)
+    with pytest.raises(RuntimeError, match="is missing"):
+        csa.lib()
+    with pytest.raises(RuntimeError, match="is missing"):
+        csa.attn_table_workspace_bytes(4, 4)
