@@ -33,9 +33,10 @@ def _run(a):
 
 
 # (B, N, Dm, H): several token blocks and a ragged tail, a batch boundary
-# inside a block, Dm a multiple of 64 (the MFMA kernel for bf16) or not
+# inside a block, Dm a multiple of 64 (the MFMA kernel for bf16) or not, and
+# head counts that fill groups of 4 heads and leave a short one (5, 9)
 SHAPES = [(1, 256, 64, 1), (3, 300, 128, 2), (2, 77, 192, 3), (1, 513, 320, 1),
-          (2, 100, 100, 2), (1, 5, 7, 1)]
+          (2, 100, 100, 2), (1, 5, 7, 1), (2, 700, 128, 5), (1, 300, 64, 9)]
 
 
 @pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
