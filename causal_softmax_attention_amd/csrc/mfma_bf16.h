@@ -35,11 +35,21 @@ __device__ __forceinline__ floatx16 mma(bf16x8_t a, bf16x8_t b, floatx16 c) {
 }
 
 // Tiles in LDS are row-major [rows][64] bf16 with chunk c of row r stored at
-// chunk c ^ swz(r): eight consecutive rows then put one chunk in eight
-// different bank groups (16-byte row reads by 8 lanes), and four consecutive
-// rows put a 32-byte chunk pair in four different 32-byte bank ranges (the
-// 8-byte transposing reads by 16 lanes).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// chunk c ^ swz(r).  LDS has 64 four-byte banks (256 bytes a clock), so a
+// row's physical chunk p lies in bank group 8 (r & 1) + p of sixteen.
+//  - A 16-byte row read serves 16 lanes a clock: sixteen consecutive rows,
+//    one logical chunk.  swz maps row bits 1-3 one-to-one onto three bits, so
+//    the eight rows of either parity take eight different chunks: no two
+//    lanes share a bank.
+//  - A transposing 8-byte read serves 32 lanes a clock: four consecutive
+//    rows (from a multiple of 4) x four chunks.  Rows r and r + 2 share a bank
+//    half; row bit 1 flips swz's top bit and so moves them to opposite
+//    halves of the eight chunks.
+// (A swizzle over row bits 0-2 alone left the row reads two-way conflicted:
+// rows r and r + 8 then collide.)
+__device__ __forceinline__ int swz(int row) {
+  return (((row >> 1) & 1) << 2) | (((row >> 2) & 1) << 1) | ((row >> 3) & 1);
+}
 __device__ __forceinline__ int lds_at(int row, int col) {
   return row * kRowElems + (((col >> 3) ^ swz(row)) << 3) + (col & 7);
 }
