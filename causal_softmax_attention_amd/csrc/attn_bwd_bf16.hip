@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
 // B with no result waited on inside a step.
 //
 // Queries stream through a 3-stage LDS ring of 64-row stages (Q, dO, and
-// -lse/scale, -delta), filled by asynchronous buffer loads.  Stage s holds
+// -lse log2(e), -delta), filled by asynchronous buffer loads.  Stage s holds
 // halves 2s and 2s+1.  Step 0 of stage s forms A(2s+1) from its own rows
 // 32.. and C(2s-1) from the previous stage's rows 32..; step 1 forms A(2s+2)
 // from the next stage's rows 0.. and C(2s) from its own rows 0...  So one
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
 }  // namespace
 
 size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N) {
-  return (size_t)heads * N * 2 * sizeof(float);  // -delta, then -lse / scale
+  return (size_t)heads * N * 2 * sizeof(float);  // -delta, then -lse log2(e)
 }
 
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,

@@ -386,7 +386,7 @@ hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __
               : mk.causal ? attn_fwd_bf16_kernel<true, false>
                           : attn_fwd_bf16_kernel<false, false>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
-  // the backward workspace: -delta per row, then -lse / scale per row
+  // the backward workspace: -delta per row, then -lse log2(e) per row
   float* ndelta = (float*)bwd_ws;
   float* nlse = ndelta ? ndelta + heads * N : nullptr;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, (int)heads,
