@@ -29,10 +29,11 @@ FLAGS = [
     "-munsafe-fp-atomics", "-fvisibility=hidden",
 ]
 
-# Per-source additions.  The dQ pass (one wave per SIMD, 512 registers) keeps
-# MFMA results in VGPRs, where the softmax reads them with plain VALU
-# instructions; the dK/dV pass needs more registers than VGPRs alone hold and
-# keeps its accumulators in AGPRs.
+# Per-source additions.  The dQ pass is built with MFMA results in VGPRs
+# (-amdgpu-mfma-vgpr-form), where its softmax reads them with plain VALU
+# instructions; at two waves per SIMD (256 registers each) no accumulator then
+# moves between AGPRs and VGPRs.  The other kernels get that placement from the
+# compiler's defaults.
 EXTRA = {
     "attn_bwd_dq_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
