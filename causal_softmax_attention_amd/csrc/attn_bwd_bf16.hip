@@ -12,17 +12,10 @@
 // Scores are recomputed from q, k and the forward's saved lse; nothing N x N is
 // stored.
 //
-// The stationary operand of the score product (K here, Q in the dQ pass) is
-// multiplied by c = scale log2(e) and rounded to bf16 once, and the per-row
-// offset is -lse_i log2(e), so a score accumulator ends as
-// c s_ij / scale - lse_i log2(e) = log2 P_ij and P is one exp2 with no
-// multiply.  The rounding of c k (at most 2^-9 of each element) moves log2 P
-// by far less than the bf16 rounding that P itself then gets.
-//
 // Three launches, no atomics (float atomics in L2 run at about one 4-byte add
 // per channel-clock on this part, far too slow for a dQ accumulated across key
 // blocks):
-//   1. prep: -delta_i and -lse_i log2(e) per row (one pass over O and dO),
+//   1. prep: -delta_i and -lse_i / scale per row (one pass over O and dO),
 //   2. dK/dV, key-stationary: a wave owns 32 keys whose K and V stay in
 //      registers as MFMA B operands; 64-query stages (Q, dO, and the two
 //      per-row values) stream through a 3-stage LDS ring filled by
@@ -60,15 +53,15 @@ constexpr int kBlk = kRowsW * kWaves;    // stationary rows per workgroup
 constexpr int kT = 64;                   // streamed rows per tile
 constexpr int kT2 = kT;                  // streamed rows per LDS stage
 
-// Per row: -delta_i = -sum_d dO_id O_id and -lse_i log2(e), the values the
+// Per row: -delta_i = -sum_d dO_id O_id and -lse_i / scale, the values the
 // score accumulators of both passes start from (so that they end as
-// dP_ij - delta_i and log2 P_ij, see above).  Eight lanes per row, 16 bytes
-// each.
+// dP_ij - delta_i and s_ij - lse_i / scale, see below).  Eight lanes per row,
+// 16 bytes each.
 __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ o,
                                                      const __bf16* __restrict__ dout,
                                                      const float* __restrict__ lse,
                                                      float* __restrict__ ndelta,
-                                                     float* __restrict__ nlse, float lse_mul,
+                                                     float* __restrict__ nlse, float inv_scale,
                                                      int64_t rows) {
   const int64_t r = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
@@ -85,7 +78,7 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
   s += __shfl_xor(s, 4);
   if (r < rows && part == 0) {
     ndelta[r] = -s;
-    nlse[r] = -lse[r] * lse_mul;
+    nlse[r] = -lse[r] * inv_scale;
   }
 }
 
@@ -93,11 +86,11 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
 //
 // A wave owns 32 keys (K, V rows in registers as MFMA B operands) and walks the
 // queries in 32-query halves.  Per half n:
-//   A(n): S' = Q (cK)^T - lse log2(e) = log2 P and dP' = dO V^T - delta
-//         (query rows x key columns), the accumulators starting from
-//         -lse log2(e) and -delta of their rows, so the offsets cost no
-//         instruction;
-//   B(n): P = exp2(S'), dS = P dP' (VALU), rounded to bf16 and packed;
+//   A(n): S' = Q K^T - lse/scale and dP' = dO V^T - delta (query rows x key
+//         columns), the accumulators starting from -lse/scale and -delta of
+//         their rows, so the offsets cost no instruction;
+//   B(n): P = exp2(c S') with c = scale log2(e), dS = P dP' (VALU), rounded to
+//         bf16 and packed;
 //   C(n): dV^T += dO^T P and dK^T += Q^T dS (the packed tiles are B operands,
 //         the transposed Q / dO rows come from ds_read_b64_tr_b16).
 // The three depend on one another in that order, so each step issues A(n+1),
@@ -105,7 +98,7 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
 // B with no result waited on inside a step.
 //
 // Queries stream through a 3-stage LDS ring of 64-row stages (Q, dO, and
-// -lse log2(e), -delta), filled by asynchronous buffer loads.  Stage s holds
+// -lse/scale, -delta), filled by asynchronous buffer loads.  Stage s holds
 // halves 2s and 2s+1.  Step 0 of stage s forms A(2s+1) from its own rows
 // 32.. and C(2s-1) from the previous stage's rows 32..; step 1 forms A(2s+2)
 // from the next stage's rows 0.. and C(2s) from its own rows 0...  So one
@@ -165,8 +158,8 @@ __device__ __forceinline__ void dkdv_scores(const QStage& st, int row0, int lane
 template <bool MASKED>
 __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[kKT], const floatx16 (&dp)[kKT],
                                              uint32_t (&pp)[kKT][8], uint32_t (&dsp)[kKT][8],
-                                             int qrow0, int kw, int lane, int causal,
-                                             int band) {
+                                             int qrow0, int kw, int lane, float c_scale,
+                                             int causal, int band) {
   const int i32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int kt = 0; kt < kKT; ++kt) {
@@ -177,7 +170,7 @@ __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[kKT], const flo
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * pr + e;
-        float p = __builtin_amdgcn_exp2f(s[kt][r]);
+        float p = __builtin_amdgcn_exp2f(s[kt][r] * c_scale);
         if (MASKED) {
           const int qi = qrow0 + acc_row(r, h);
           p = (causal && key > qi) || (band && qi - key >= band) ? 0.f : p;
@@ -214,13 +207,13 @@ __device__ __forceinline__ void dkdv_accum(const QStage& st, int row0, int lane,
 // is qrow0, C(n-1) from (sc, rc).  SKIP_C: there is no half n-1.
 template <bool MASKED, bool SKIP_C>
 __device__ __forceinline__ void dkdv_step(const QStage& sa, int ra, const QStage& sc, int rc,
-                                          int qrow0, int kw, int lane, int causal,
+                                          int qrow0, int kw, int lane, float c_scale, int causal,
                                           int band, const bf16x8_t (&kop)[kKT][4],
                                           const bf16x8_t (&vop)[kKT][4], DkdvPipe& pipe,
                                           floatx16 (&dkacc)[2][kKT], floatx16 (&dvacc)[2][kKT]) {
   uint32_t pp[kKT][8], dsp[kKT][8];
   if (!SKIP_C) dkdv_accum(sc, rc, lane, pipe.pp, pipe.dsp, dkacc, dvacc);
-  dkdv_softmax<MASKED>(pipe.s, pipe.dp, pp, dsp, qrow0, kw, lane, causal, band);
+  dkdv_softmax<MASKED>(pipe.s, pipe.dp, pp, dsp, qrow0, kw, lane, c_scale, causal, band);
   dkdv_scores(sa, ra, lane, kop, vop, pipe.s, pipe.dp);
 #pragma unroll
   for (int kt = 0; kt < kKT; ++kt)
@@ -253,7 +246,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   const int kw = kb * kBlk + wave * kRowsW;  // first key of this wave
 
   // stationary B operands: lane holds X[key kw + 32 kt + i32][16 kk + 8 h .. +7]
-  // (K multiplied by c = scale log2(e))
   bf16x8_t kop[kKT][4], vop[kKT][4];
 #pragma unroll
   for (int kt = 0; kt < kKT; ++kt) {
@@ -265,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
         a = ldg16(k + base + (size_t)key * kD + 16 * kk + 8 * h);
         b = ldg16(v + base + (size_t)key * kD + 16 * kk + 8 * h);
       }
-      kop[kt][kk] = scale_bf16x8(__builtin_bit_cast(bf16x8_t, a), c_scale);
+      kop[kt][kk] = __builtin_bit_cast(bf16x8_t, a);
       vop[kt][kk] = __builtin_bit_cast(bf16x8_t, b);
     }
   }
@@ -298,11 +290,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   auto stage = [&](auto masked, auto first, QStage& cur, QStage& nxt, QStage& prv, int s) {
     constexpr bool M = decltype(masked)::value, F = decltype(first)::value;
     const int q0 = qstart + s * kT2;
-    dkdv_step<M, F>(cur, 32, prv, 32, q0, kw, lane, causal, band, kop, vop, pipe,
+    dkdv_step<M, F>(cur, 32, prv, 32, q0, kw, lane, c_scale, causal, band, kop, vop, pipe,
                     dkacc, dvacc);
     wait_vm_barrier<0>();  // stage s + 1 has landed; every wave is done with prv
     if (s + 2 < nst) issue(prv, s + 2);
-    dkdv_step<M, false>(nxt, 0, cur, 0, q0 + 32, kw, lane, causal, band, kop, vop,
+    dkdv_step<M, false>(nxt, 0, cur, 0, q0 + 32, kw, lane, c_scale, causal, band, kop, vop,
                         pipe, dkacc, dvacc);
   };
   // stages 0 and 1 hold the block's diagonal (masked body); later stages lie
@@ -383,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
 }  // namespace
 
 size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N) {
-  return (size_t)heads * N * 2 * sizeof(float);  // -delta, then -lse log2(e)
+  return (size_t)heads * N * 2 * sizeof(float);  // -delta, then -lse / scale
 }
 
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
@@ -399,7 +391,7 @@ hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, co
   if (!prepared) {  // else the forward already wrote both per-row values (dO = O)
     if (hipError_t e = mark(tm.start[kTimerBwdPre], stream)) return e;
     hipLaunchKernelGGL(bwd_prep_bf16, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, o,
-                       dout, lse, ndelta, nlse, (float)1.4426950408889634, rows);
+                       dout, lse, ndelta, nlse, (float)(1.0 / scale), rows);
     if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
   }
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;

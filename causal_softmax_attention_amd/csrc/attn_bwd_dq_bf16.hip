@@ -1,9 +1,8 @@
 // dQ of the bfloat16 causal attention backward on gfx950 MFMA: the
 // query-stationary pass (a wave owns 32 queries; K, V stream through LDS).
-// The per-row values it reads, -delta_i and -lse_i log2(e), come from the
+// The per-row values it reads, -delta_i and -lse_i / scale, come from the
 // backward's prep kernel (attn_bwd_bf16.hip), which also documents the
-// gradient formulas and the scaled score operand (here the stationary Q
-// times scale log2(e), rounded to bf16 once) (pages: "Show HN: automatic deduction of FlashAttention
+// gradient formulas (pages: "Show HN: automatic deduction of FlashAttention
 // kernel from 25 lines of SQL", the GRADIENT statement).
 #include "common.h"
 #include "launch.h"
@@ -28,14 +27,15 @@ constexpr int kT2 = kT;                  // keys per LDS stage
 // halves of 32 keys: the second half's S^T / dP^T MFMAs are issued before the
 // first half's exp / VALU work, and the first half's dQ MFMAs before the
 // second half's, so each wave always has independent MFMA and VALU work in
-// flight.  The score accumulators start from -lse log2(e) and -delta of their
-// query (one per lane), as in the dK/dV pass, so P = exp2 of the first.  MASKED: the tile holds absent
+// flight.  The score accumulators start from -lse/scale and -delta of their
+// query (one per lane), as in the dK/dV pass.  MASKED: the tile holds absent
 // pairs (past the wave's diagonal or a window's start, or past the end of the
 // sequence), which get weight 0 (a select, not a branch).
 template <bool MASKED>
 __device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[kQT], const floatx16 (&dp)[kQT],
                                                 uint32_t (&dsp)[kQT][8], int kt, int k0, int qw,
-                                                int N, int i32, int h, int causal, int band) {
+                                                int N, int i32, int h, float c_scale, int causal,
+                                                int band) {
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     const int qi = qw + 32 * qt + i32;
@@ -45,7 +45,7 @@ __device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[kQT], const 
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int r = 2 * pr + e;
-        float p = __builtin_amdgcn_exp2f(s[qt][r]);
+        float p = __builtin_amdgcn_exp2f(s[qt][r] * c_scale);
         if (MASKED) {
           const int key = k0 + 32 * kt + acc_row(r, h);
           p = (key >= N || (causal && key > qi) || (band && qi - key >= band)) ? 0.f : p;
@@ -88,7 +88,8 @@ __device__ __forceinline__ void dq_half_scores(const __bf16* ks, const __bf16* v
 
 template <bool MASKED>
 __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int lane, int k0,
-                                        int qw, int N, const bf16x8_t (&qop)[kQT][4], const bf16x8_t (&oop)[kQT][4],
+                                        int qw, int N, float c_scale,
+                                        const bf16x8_t (&qop)[kQT][4], const bf16x8_t (&oop)[kQT][4],
                                         const float (&nls)[kQT], const float (&ndl)[kQT],
                                         floatx16 (&dqacc)[2][kQT], int causal, int band) {
   const int i32 = lane & 31, h = lane >> 5;
@@ -101,7 +102,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) ktr0[half][dt] = read_tr(ks, lane, half, 32 * dt);
   dq_half_scores(ks, vs, 1, i32, h, qop, oop, nls, ndl, s1, dp1);
-  dq_half_softmax<MASKED>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, causal, band);
+  dq_half_softmax<MASKED>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale, causal, band);
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -113,7 +114,7 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt)
         dqacc[dt][qt] = mma(ktr0[half][dt], chunk_op(dsp0[qt], half), dqacc[dt][qt]);
-  dq_half_softmax<MASKED>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, causal, band);
+  dq_half_softmax<MASKED>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale, causal, band);
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -147,8 +148,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
   const int qw = qb * kBlk + wave * kRowsW;
   const int wq_last = min(qw + kRowsW, N) - 1;
 
-  // stationary B operands of S^T = K (cQ)^T and dP^T = V dO^T (c = scale log2(e));
-  // per-lane -lse log2(e), -delta
+  // stationary B operands of S^T = K Q^T and dP^T = V dO^T; per-lane -lse/scale, -delta
   bf16x8_t qop[kQT][4], oop[kQT][4];
   float nls[kQT], ndl[kQT];
 #pragma unroll
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
         a = ldg16(q + base + (size_t)qi * kD + 16 * kk + 8 * h);
         b = ldg16(dout + base + (size_t)qi * kD + 16 * kk + 8 * h);
       }
-      qop[qt][kk] = scale_bf16x8(__builtin_bit_cast(bf16x8_t, a), c_scale);
+      qop[qt][kk] = __builtin_bit_cast(bf16x8_t, a);
       oop[qt][kk] = __builtin_bit_cast(bf16x8_t, b);
     }
     nls[qt] = qi < N ? nlseg[(size_t)head * N + qi] : 0.f;
@@ -193,10 +193,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
       if (k0 <= whi && k0 + kT - 1 >= wlo) {
         // masked: some pair of the tile is absent for some query of the wave
         if ((causal && k0 + kT - 1 > qw) || (k0 + kT > N) || (band && k0 < qw + kRowsW - band))
-          dq_tile<true>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N,
+          dq_tile<true>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale,
                         qop, oop, nls, ndl, dqacc, causal, band);
         else
-          dq_tile<false>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N,
+          dq_tile<false>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale,
                          qop, oop, nls, ndl, dqacc, causal, band);
       }
     }

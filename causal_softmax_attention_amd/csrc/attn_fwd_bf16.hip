@@ -37,13 +37,6 @@
 // instruction on a max.  m_ref starts at -inf, so the first tile always takes
 // the exact path.  Products p * v are then bounded by 2^8 |v|.
 //
-// Scaled scores: Q (the stationary operand) is multiplied by c = scale log2(e)
-// and rounded to bf16 once, and the score MFMAs start from a tile holding
-// -m_ref in every register of the lane, so they end as s*c - m_ref and the
-// common path takes exp2 of the accumulator with no other instruction.  The
-// rounding of c q (at most 2^-9 of each element) moves the exponent by far
-// less than the bf16 rounding that the weight itself then gets.
-//
 // Absent rows with non-finite V: a masked pair must contribute nothing, but
 // the MFMA would form 0 * inf = NaN.  On a masked tile each wave scans the V
 // tile; if it holds any inf/NaN, that tile's P V is formed by a select-based
@@ -87,26 +80,22 @@ __device__ __forceinline__ bool all_finite_bf16x8(uint4 w) {
   return (bad(w.x) | bad(w.y) | bad(w.z) | bad(w.w)) == 0;
 }
 
-// Weights of one 64-key tile, exp2 of the scores less `shift` (SHIFTED) or
-// of the scores as they are, packed to bf16 pairs in B-operand order; returns
-// the lane's sums of the rounded weights per query column.
-template <bool SHIFTED>
-__device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][kQT], const float (&shift)[kQT],
-                                             uint32_t (&p)[kQT][2][8], float (&part)[kQT]) {
+// Weights of one 64-key tile against the lane's reference max, packed to
+// bf16 pairs in B-operand order; returns the lane's sums of the rounded
+// weights per query column.
+__device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][kQT], float c_scale,
+                                             const float (&mref)[kQT], uint32_t (&p)[kQT][2][8],
+                                             float (&part)[kQT]) {
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
+    const float nm = -mref[qt];
     float acc = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int pr = 0; pr < 8; ++pr) {
-        float x = s[kt][qt][2 * pr], y = s[kt][qt][2 * pr + 1];
-        if (SHIFTED) {
-          x -= shift[qt];
-          y -= shift[qt];
-        }
-        const float a = __builtin_amdgcn_exp2f(x);
-        const float b = __builtin_amdgcn_exp2f(y);
+        const float a = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][2 * pr], c_scale, nm));
+        const float b = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][2 * pr + 1], c_scale, nm));
         p[qt][kt][pr] = pack_bf16(a, b);
         acc = sum_bf16_pair(p[qt][kt][pr], acc);
       }
@@ -116,28 +105,15 @@ __device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][kQT], const 
 
 // One key tile for one wave (32 queries x 64 keys).  MASKED: the tile crosses
 // the wave's diagonal or the end of the sequence.
-// The score accumulators start from a tile holding -mbase[qt] in every
-// register (formed per tile: 16 moves, against 32 multiply-adds saved);
-// mbase equals mref once the lane has seen a present pair (before that mref
-// is kRefInit, mbase 0, and every tile takes the exact path).
 template <bool MASKED>
 __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __bf16* pscr,
-                                         int lane, int k0, int qw, int N, int causal, int band,
-                                         const bf16x8_t (&qop)[kQT][4], floatx16 (&oacc)[2][kQT],
-                                         float (&mref)[kQT], float (&mbase)[kQT],
+                                         int lane, int k0, int qw, int N, float c_scale,
+                                         int causal, int band, const bf16x8_t (&qop)[kQT][4],
+                                         floatx16 (&oacc)[2][kQT], float (&mref)[kQT],
                                          float (&lsum)[kQT]) {
   const int i32 = lane & 31, h = lane >> 5;
-  // ---- S^T = K (cQ)^T - mbase: s[kt][qt] holds keys k0 + 32 kt + acc_row(r, h),
-  // query column
+  // ---- S^T = K Q^T: s[kt][qt] holds keys k0 + 32 kt + acc_row(r, h), query column
   floatx16 s[2][kQT];
-  floatx16 cinit[kQT];
-#pragma unroll
-  for (int qt = 0; qt < kQT; ++qt) {
-    float nb = -mbase[qt];
-    asm volatile("" : "+v"(nb));  // formed here, not held across the loop
-#pragma unroll
-    for (int r = 0; r < 16; ++r) cinit[qt][r] = nb;
-  }
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     bf16x8_t kop[4];
@@ -145,9 +121,9 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
     for (int kk = 0; kk < 4; ++kk) kop[kk] = read_row8(ks, 32 * kt + i32, 16 * kk + 8 * h);
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
-      floatx16 acc = mma(kop[0], qop[qt][0], cinit[qt]);
+      floatx16 acc = floatx16{};
 #pragma unroll
-      for (int kk = 1; kk < 4; ++kk) acc = mma(kop[kk], qop[qt][kk], acc);
+      for (int kk = 0; kk < 4; ++kk) acc = mma(kop[kk], qop[qt][kk], acc);
       s[kt][qt] = acc;
     }
   }
@@ -167,12 +143,11 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
   // ---- weights against the reference max, exact max only when needed
   uint32_t p[kQT][2][8];
   float part[kQT];
-  tile_weights<false>(s, mbase, p, part);
+  tile_weights(s, c_scale, mref, p, part);
   bool over = false;
 #pragma unroll
-  for (int qt = 0; qt < kQT; ++qt) over |= !(part[qt] <= kTau) || mbase[qt] != mref[qt];
+  for (int qt = 0; qt < kQT; ++qt) over |= !(part[qt] <= kTau);
   if (__any(over)) {
-    float shift[kQT];
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt) {
       float mx = -__builtin_inff();
@@ -181,7 +156,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][qt][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mref[qt], mx + mbase[qt]);
+      const float mnew = fmaxf(mref[qt], mx * c_scale);
       if (mnew != mref[qt]) {
         const float alpha = __builtin_amdgcn_exp2f(mref[qt] - mnew);  // 0 from kRefInit
         lsum[qt] *= alpha;
@@ -191,12 +166,8 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
           for (int r = 0; r < 16; ++r) oacc[dt][qt][r] *= alpha;
         mref[qt] = mnew;
       }
-      shift[qt] = mref[qt] - mbase[qt];
     }
-    tile_weights<true>(s, shift, p, part);
-#pragma unroll
-    for (int qt = 0; qt < kQT; ++qt)
-      if (mref[qt] > 0.5f * kRefInit) mbase[qt] = mref[qt];  // the next tiles start from -mref
+    tile_weights(s, c_scale, mref, p, part);
   }
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) lsum[qt] += part[qt];
@@ -258,7 +229,7 @@ template <bool CAUSAL, bool BANDED>
 __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale,
-    int band_arg, float* __restrict__ ndelta, float* __restrict__ nlse, float lse_mul) {
+    int band_arg, float* __restrict__ ndelta, float* __restrict__ nlse, float inv_scale) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
@@ -276,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
   const int ntiles = (kend + kBc - 1) / kBc;
   const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
 
-  // Q operand: lane holds c q[qw + 32 qt + i32][16 kk + 8 h .. +7], c = scale log2(e)
+  // Q operand: lane holds q[qw + 32 qt + i32][16 kk + 8 h .. +7]
   bf16x8_t qop[kQT][4];
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
@@ -285,7 +256,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
     for (int kk = 0; kk < 4; ++kk) {
       uint4 w = make_uint4(0, 0, 0, 0);
       if (qi < N) w = ldg16(q + base + (size_t)qi * kD + 16 * kk + 8 * h);
-      qop[qt][kk] = scale_bf16x8(__builtin_bit_cast(bf16x8_t, w), c_scale);
+      qop[qt][kk] = __builtin_bit_cast(bf16x8_t, w);
     }
   }
   floatx16 oacc[2][kQT];  // [dt][qt]: O^T tile, lane holds query column
@@ -296,11 +267,10 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
   // reference exponents start finite, so a tile whose pairs are all absent for
   // a lane gives it weights exp2(-inf) = 0, and its first present pair takes the
   // exact path (the weight overflows against kRefInit)
-  float mref[kQT], mbase[kQT], lsum[kQT];
+  float mref[kQT], lsum[kQT];
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     mref[qt] = kRefInit;
-    mbase[qt] = 0.f;
     lsum[qt] = 0.f;
   }
 
@@ -317,11 +287,11 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
     if (k0 <= whi && k0 + kBc - 1 >= wlo) {
       // masked: some pair of the tile is absent for some query of the wave
       if ((causal && k0 + kBc - 1 > qw) || (k0 + kBc > N) || (band && k0 < qw + kQW - band))
-        fwd_tile<true>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, causal, band, qop, oacc, mref,
-                       mbase, lsum);
+        fwd_tile<true>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band, qop,
+                       oacc, mref, lsum);
       else
-        fwd_tile<false>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, causal, band, qop, oacc, mref,
-                        mbase, lsum);
+        fwd_tile<false>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band, qop,
+                        oacc, mref, lsum);
     }
     if (pre) wait_vm_barrier<2 * kBc / (8 * kWaves)>();
     else wait_vm_barrier<0>();
@@ -338,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
 
   // ---- epilogue: l over both lane halves, O = O^T / l, lse = (m + log2 l) ln 2.
   // With ndelta given (the loss sum(o^2)/2, so dO = O), also the backward's
-  // per-row values from the stored bf16 row: -delta_i = -|o_i|^2 and -lse_i log2(e).
+  // per-row values from the stored bf16 row: -delta_i = -|o_i|^2 and -lse_i / scale.
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     const int qi = qw + 32 * qt + i32;
@@ -367,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
         sq += __shfl_xor(sq, 32);  // the partner lane holds the row's other 32 features
         if (h == 0) {
           ndelta[(size_t)head * N + qi] = -sq;
-          nlse[(size_t)head * N + qi] = -lse_i * lse_mul;  // -lse log2(e), as the backward's prep
+          nlse[(size_t)head * N + qi] = -lse_i * inv_scale;
         }
       }
     }
@@ -386,11 +356,11 @@ hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __
               : mk.causal ? attn_fwd_bf16_kernel<true, false>
                           : attn_fwd_bf16_kernel<false, false>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
-  // the backward workspace: -delta per row, then -lse log2(e) per row
+  // the backward workspace: -delta per row, then -lse / scale per row
   float* ndelta = (float*)bwd_ws;
   float* nlse = ndelta ? ndelta + heads * N : nullptr;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, (int)heads,
-                     (int)N, nqb, c, mk.band, ndelta, nlse, (float)1.4426950408889634);
+                     (int)N, nqb, c, mk.band, ndelta, nlse, (float)(1.0 / scale));
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }

@@ -39,7 +39,7 @@ struct Mask {
 // Every forward launcher takes `bwd_ws`: null, or the backward workspace, which
 // the forward then fills with the per-row values of the loss sum(o^2)/2
 // (dO = O) so that the backward launchers can run `prepared` (without their
-// first, per-row kernel).  Layouts: bfloat16 -delta_i then -lse_i log2(e)
+// first, per-row kernel).  Layouts: bfloat16 -delta_i then -lse_i / scale
 // (float each); float32 / float64 delta_i in the accumulation type.
 
 // Row-per-group kernels (attn_rowwise.hip): forward and backward of `heads`
@@ -71,7 +71,7 @@ hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __
                            void* bwd_ws, hipStream_t stream, const Timers& tm);
 
 // bfloat16 backward on MFMA tiles (attn_bwd_bf16.hip); the workspace holds two floats
-// per row (-delta and -lse log2(e)).
+// per row (-delta and -lse / scale).
 size_t bwd_workspace_bytes_bf16(int64_t heads, int64_t N);
 hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, const __bf16* o,
                            const __bf16* dout, const float* lse, __bf16* dq, __bf16* dk,

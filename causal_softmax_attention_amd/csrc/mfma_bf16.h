@@ -71,14 +71,6 @@ __device__ __forceinline__ bf16x8_t read_tr(const __bf16* tile, int lane, int c,
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// An operand times c, each element rounded back to bf16 (nearest even).
-__device__ __forceinline__ bf16x8_t scale_bf16x8(bf16x8_t x, float c) {
-  bf16x8_t y;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = (__bf16)((float)x[e] * c);
-  return y;
-}
-
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   bf16x2_t p = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, p);

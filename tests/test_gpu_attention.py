@@ -80,6 +80,29 @@ def test_small_fwd_bwd(dtype, shape):
     _check_bwd(a, grads)
 
 
+# (dtype, qk_mult).  At qk_mult 6 the scores reach about +-100, and float32's
+# own rounding of a 64-term dot product (about 1e-4 of the score's terms) moves
+# the weights by more than the float32 tolerance of 1e-5: that case is float32
+# arithmetic, not the kernel, so it is checked in float64 and bfloat16 only.
+PEAKED = [("f64", 3.0), ("f32", 3.0), ("bf16", 3.0), ("f64", 6.0), ("bf16", 6.0)]
+
+
+@pytest.mark.parametrize("dtype,qk_mult", PEAKED, ids=lambda x: str(x))
+def test_peaked_scores(dtype, qk_mult):
+    """q and k drawn N(0, qk_mult^2): scores qk_mult^2 times those of the unit
+    workload, so the softmax is peaked and any rounding of the score operands
+    moves the weights in proportion to the score.  Fwd and bwd checked in full
+    against the oracle, at the same tolerances."""
+    B, H, N = 1, 2, 1000
+    a = inp.attention_inputs(131, B, H, N, dtype, qk_mult=qk_mult)
+    note(f"peaked scores {dtype} qk_mult={qk_mult} B={B} H={H} N={N}")
+    q, k, v = (to_dev(getattr(a, x), dtype) for x in "qkv")
+    o, lse = run_fwd(q, k, v, S)
+    _check_fwd(a, o, lse)
+    grads = run_bwd(q, k, v, o, o, lse, S)
+    _check_bwd(a, grads)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_head_groups(dtype):
     """21 heads: an XCD's heads (workgroup b runs on XCD b % 8) come in groups
