@@ -76,6 +76,25 @@ def test_mask_fwd_bwd(dtype, mask, window, shape):
     _check(a, o, lse, grads, mask, window)
 
 
+@pytest.mark.parametrize("dtype", ["f64", "bf16"])
+@pytest.mark.parametrize("mask,window", [("full", 0), ("window", 37), ("window", 400)],
+                         ids=lambda x: str(x))
+def test_mask_peaked_scores(dtype, mask, window):
+    """q and k drawn N(0, 36) (scores 36 times the unit workload's): a peaked
+    softmax under the other predicates, where a window's first key tile can
+    hold a lane's largest score after tiles of smaller ones (the forward's
+    reference exponent must then move).  float32 is left out as in
+    test_gpu_attention.test_peaked_scores: its own rounding of such scores
+    exceeds its tolerance."""
+    B, H, N = 1, 2, 777
+    a = inp.attention_inputs(600 + window, B, H, N, dtype, qk_mult=6.0)
+    note(f"peaked {mask} window={window} {dtype} B={B} H={H} N={N}")
+    q, k, v = (to_dev(getattr(a, x), dtype) for x in "qkv")
+    o, lse = run_fwd(q, k, v, S, mask=mask, window=window)
+    grads = run_bwd(q, k, v, o, o, lse, S, mask=mask, window=window)
+    _check(a, o, lse, grads, mask, window)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_causal_entry_points_agree(dtype):
     """attn_fwd / attn_bwd with the causal mask are attn_causal_fwd / _bwd, bit for bit."""
