@@ -29,8 +29,10 @@
 //     only the diagonal tile and the ragged tail (keys >= N) are masked, by
 //     setting those scores to -inf (an absent pair gets weight exactly 0).
 //
-// Lazy max: the row max only keeps exp from overflowing; it cancels from the
-// ratio (the page's remark on the window spelling).  Weights are therefore
+// Lazy max: any offset common to a row's scores drops out of w / z, so the
+// subtracted value need not be the exact maximum; it only has to keep the
+// exponentials in float32 range (the demo script makes the same point beside
+// its window spelling).  Weights are therefore
 // taken as exp2(s*c - m_ref) against a reference m_ref, and a tile is redone
 // with its exact max (rescaling the accumulators) only when some weight would
 // exceed 2^8 - detected from the lane's tile sum, so the common path spends no

@@ -42,11 +42,17 @@ oracle takes the closed-form chain rule through the same definitions:
 * delta_i = sum_j P_ij dP_ij,  dS_ij = P_ij (dP_ij - delta_i),
 * dQ_i = scale * sum_{j<=i} dS_ij k_j,  dK_j = scale * sum_{i>=j} dS_ij q_i.
 
-The row max is a constant to this derivative: it cancels from w / z, so its own
-gradient sums to zero (the page's comment above ``ATTENTION_WINDOW``).  With
-``route_max=True`` the backward also adds the term that flows through the max
-to the argmax pair, as an autodiff of the window would, which must change
-nothing beyond rounding.
+Adding one constant to every score of a row leaves every ratio w / z of that
+row unchanged, so the loss does not depend on m_i and the derivative through
+it is zero; the oracle treats m_i as a constant (the demo script says as much
+beside its window spelling).  With ``route_max=True`` the backward also adds
+the term that reaches the argmax pair through m_i, as a mechanical
+differentiation of the window would, which must change nothing beyond
+rounding.
+
+``forward`` and ``backward`` apply the per-head functions to every (b, h)
+head of [B, H, N, D] arrays, optionally on a thread pool over heads (NumPy
+releases the interpreter lock inside its kernels).
 
 Rows are processed in blocks of ``block`` queries only to bound memory: every
 row's whole score vector is materialised and reduced exactly (two passes: max,
@@ -122,12 +128,12 @@ def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
         r1 = min(n, r0 + block)
         nc = _key_cols(r1, n, mask)
         present = _present(r0, r1, nc, mask, window)
-        s = (q[r0:r1] @ k[:nc].T) * scale                       # scores
-        m = np.max(np.where(present, s, -np.inf), axis=1)       # MAX(s) OVER (PARTITION BY i)
+        s = (q[r0:r1] @ k[:nc].T) * scale                       # s_ij for every (i, j) of the block
+        m = np.max(np.where(present, s, -np.inf), axis=1)       # m_i over present pairs only
         with np.errstate(invalid="ignore", over="ignore"):
-            w = np.where(present, np.exp(s - m[:, None]), 0.0)  # exp(s - max)
-        z = w.sum(axis=1)                                       # SUM(w) GROUP BY i
-        o[r0:r1] = _sum_present(w / z[:, None], present, v[:nc])  # SUM(w / z * v)
+            w = np.where(present, np.exp(s - m[:, None]), 0.0)  # w_ij, 0 where no pair exists
+        z = w.sum(axis=1)                                       # z_i
+        o[r0:r1] = _sum_present(w / z[:, None], present, v[:nc])  # o_i = sum_j (w_ij / z_i) v_j
         lse[r0:r1] = m + np.log(z)
         m_all[r0:r1] = m
         z_all[r0:r1] = z
@@ -137,43 +143,49 @@ def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 def forward_head_relational(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                             scale: float = DEFAULT_SCALE, spelling: str = "group by",
                             mask: str = "causal", window: int = 0):
-    """The view as relations in long format, one row per existing (i, j) pair.
+    """The same attention computed over an explicit list of the pairs that
+    exist, the way the demo script's two views (``ATTENTION_WINDOW`` and
+    ``ATTENTION_GROUP_BY``) treat their join: one record per pair (i, j), and
+    every per-row quantity an aggregate over the records of row i.
 
-    ``spelling="group by"`` computes each row's max as a GROUP BY and joins it
-    back to the pairs; ``"window"`` takes the max over each pair's partition by
-    sorting the pair rows by i.  Aggregates are scatter-adds over the pair
-    rows, so absent pairs are never touched.  Quadratic memory: small N only.
+    The two spellings differ only in how the row maximum reaches each record:
+    ``"group by"`` reduces the records to one maximum per row and looks it up
+    again by the record's row; ``"window"`` sorts the records by row and takes
+    the maximum inside each row's run.  Records exist only for present pairs,
+    so an absent pair is never touched.  Memory is quadratic: small N only.
     Returns (o, lse)."""
     _check_mask(mask, window)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     n, d = q.shape
-    ii, jj = np.nonzero(_present(0, n, n, mask, window))        # q JOIN k WHERE <predicate>
-    s = np.einsum("pd,pd->p", q[ii], k[jj]) * scale               # SUM(q.x * k.x) GROUP BY q.t, k.t
+    rows, cols = np.nonzero(_present(0, n, n, mask, window))  # the pair records (i, j)
+    s = np.einsum("pd,pd->p", q[rows], k[cols]) * scale      # one score per record
     if spelling == "group by":
-        row_max = np.full(n, -np.inf)
-        np.maximum.at(row_max, ii, s)                              # SELECT i, MAX(s) GROUP BY i
-        m = row_max[ii]                                            # JOIN row_max ON s.i = r.i
+        best = np.full(n, -np.inf)
+        np.maximum.at(best, rows, s)                           # largest score of each row
+        m = best[rows]                                         # ... handed back to its records
     elif spelling == "window":
-        order = np.lexsort((jj, ii))
-        bounds = np.searchsorted(ii[order], np.arange(n + 1))
+        order = np.lexsort((cols, rows))                       # records grouped by row
+        starts = np.searchsorted(rows[order], np.arange(n + 1))
         m = np.empty_like(s)
-        for i in range(n):                                         # one partition per i
-            idx = order[bounds[i]:bounds[i + 1]]
-            m[idx] = s[idx].max()
+        for i in range(n):
+            run = order[starts[i]:starts[i + 1]]
+            m[run] = s[run].max()
     else:
         raise ValueError(spelling)
-    w = np.exp(s - m)
+    w = np.exp(s - m)                                          # record weights
     z = np.zeros(n)
-    np.add.at(z, ii, w)                                            # norm: SUM(w) GROUP BY i
+    np.add.at(z, rows, w)                                      # z_i: sum of row i's weights
     o = np.zeros((n, d))
-    np.add.at(o, ii, (w / z[ii])[:, None] * v[jj])                 # SUM(w / z * v) GROUP BY i, d
-    row_max = np.full(n, -np.inf)
-    np.maximum.at(row_max, ii, s)
-    return o, row_max + np.log(z)
+    np.add.at(o, rows, (w / z[rows])[:, None] * v[cols])       # o_i: weighted sum of its values
+    best = np.full(n, -np.inf)
+    np.maximum.at(best, rows, s)
+    return o, best + np.log(z)
 
 
 def loss(o: np.ndarray) -> float:
-    """SUM(x * x) / 2 over every output value."""
+    """Half the sum of the squares of every output value (the loss of the
+    demo script's gradient statement and of its JAX ``loss()``), so that the
+    loss's gradient with respect to o is o itself."""
     o = np.asarray(o, dtype=np.float64)
     return float(np.sum(o * o) / 2)
 

@@ -1,8 +1,8 @@
 """Pins for the oracle: checks against what the pages and the mathematics fix.
 
 Each ``check_*`` takes the oracle as a module-like object ``orc`` (with
-``forward_head``, ``forward_head_relational``, ``backward_head`` and
-``nw_average``) and raises ``AssertionError`` on failure.  ``test_oracle.py``
+``forward_head``, ``forward_head_relational``, ``backward_head``, ``loss``,
+``forward``, ``backward`` and ``nw_average``) and raises ``AssertionError`` on failure.  ``test_oracle.py``
 runs them on the real oracle; ``test_oracle_mutants.py`` runs them on copies of
 the oracle with a mistake planted, and requires each mistake to fail one.
 
@@ -382,6 +382,85 @@ def check_mask_grad_invariants(orc):
     assert np.abs(dq[0]).max() > 1e-3 * np.abs(dq).max()
 
 
+# ------------------------------------------------------------------- loss --
+# The loss of the demo script's gradient statement and of its JAX loss():
+# half the sum of the squared outputs.
+
+def check_loss_values(orc):
+    """A hand-worked value (3^2 + 4^2 + 0^2 + (-1)^2) / 2 = 13, and two closed
+    forms through the forward: one token gives o_0 = v_0, so the loss is
+    |v_0|^2 / 2; Q = 0 gives prefix means, so it is sum_i |mean(v_0..v_i)|^2 / 2."""
+    assert orc.loss(np.array([[3.0, 4.0], [0.0, -1.0]])) == 13.0
+    rng = _rng(80)
+    q, k, v = (rng.normal(size=(1, 64)) for _ in range(3))
+    assert abs(orc.loss(orc.forward_head(q, k, v, S)[0]) - 0.5 * float(v[0] @ v[0])) \
+        < 1e-14 * float(v[0] @ v[0])
+    n = 40
+    k, v = rng.normal(size=(n, 64)), rng.normal(size=(n, 64))
+    means = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    want = 0.5 * float(np.sum(means * means))
+    assert abs(orc.loss(orc.forward_head(np.zeros((n, 64)), k, v, S, block=16)[0]) - want) \
+        < 1e-13 * want
+
+
+def check_loss_brute(orc):
+    """Against the 50-digit brute-force loss of the same tiny heads."""
+    for n, d, seed in ((7, 5, 81), (3, 64, 82)):
+        rng = _rng(seed)
+        q, k, v = (rng.normal(size=(n, d)) for _ in range(3))
+        want = float(brute.loss_mp(brute._mp(q), brute._mp(k), brute._mp(v), brute.mpmath.mpf(S)))
+        got = orc.loss(orc.forward_head(q, k, v, S, block=3)[0])
+        assert abs(got - want) < 1e-14 * abs(want), (n, d, got, want)
+
+
+def check_loss_gradient(orc):
+    """The loss is the one the backward differentiates: central differences of
+    loss(forward(q, k, v)) match backward_head with dO = O (itself pinned to
+    50-digit differences above)."""
+    rng = _rng(83)
+    n = 12
+    q, k, v = (rng.normal(size=(n, 64)) for _ in range(3))
+    grads = orc.backward_head(q, k, v, None, S, block=5)
+    h = 1e-6
+    for which, g in enumerate(grads):
+        for r, c in ((0, 0), (5, 31), (11, 63), (8, 2)):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][r, c] += h
+            lp = orc.loss(orc.forward_head(*args, S)[0])
+            args[which][r, c] -= 2 * h
+            lm = orc.loss(orc.forward_head(*args, S)[0])
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - g[r, c]) < 2e-7 * max(1.0, np.abs(g).max()), (which, r, c, fd, g[r, c])
+
+
+# ---------------------------------------------------------- batched heads --
+
+def check_batched_heads(orc):
+    """The [B, H, N, D] wrappers treat every (b, h) head on its own: each
+    output head equals the 50-digit brute force of that head's inputs (heads
+    all differ), with and without the thread pool over heads."""
+    rng = _rng(84)
+    b, h, n, d = 2, 2, 4, 3
+    q, k, v = (rng.normal(size=(b, h, n, d)) for _ in range(3))
+    for workers in (None, 3):
+        o, lse = orc.forward(q, k, v, S, workers=workers)
+        grads = orc.backward(q, k, v, None, S, workers=workers)
+        for bi in range(b):
+            for hi in range(h):
+                bo, bl = brute.attention(q[bi, hi], k[bi, hi], v[bi, hi], S)
+                assert rel_err(o[bi, hi], brute.to_np(bo)) < 1e-14, (workers, bi, hi)
+                assert rel_err(lse[bi, hi], brute.to_np(bl)) < 1e-14, (workers, bi, hi)
+                want = brute.grad_fd(q[bi, hi], k[bi, hi], v[bi, hi], S)
+                for name, g, w in zip("qkv", grads, want):
+                    assert rel_err(g[bi, hi], w) < 1e-12, ("d" + name, workers, bi, hi)
+        # an explicit upstream gradient: dO = O reproduces the default, and the
+        # gradients are linear in dO
+        for scale_d in (1.0, -2.0):
+            given = orc.backward(q, k, v, scale_d * o, S, workers=workers)
+            for g, w in zip(given, grads):
+                assert rel_err(g, scale_d * w) < 1e-14, (workers, scale_d)
+
+
 ATTENTION_FORWARD_CHECKS = [check_brute_force, check_worked_example, check_token0,
                             check_equal_scores, check_rows_sum_to_one, check_prefix,
                             check_linearity, check_k_shift, check_inf_rule, check_spellings_agree]
@@ -391,4 +470,7 @@ NW_CHECKS = [check_nw_brute, check_nw_special, check_nw_shift]
 MASK_CHECKS = [check_mask_brute_force, check_window_limits, check_mask_equal_scores,
                check_full_key_permutation, check_mask_spellings, check_mask_grad_brute_fd,
                check_mask_grad_invariants]
-ALL_CHECKS = ATTENTION_FORWARD_CHECKS + ATTENTION_BACKWARD_CHECKS + NW_CHECKS + MASK_CHECKS
+LOSS_CHECKS = [check_loss_values, check_loss_brute, check_loss_gradient]
+BATCH_CHECKS = [check_batched_heads]
+ALL_CHECKS = (ATTENTION_FORWARD_CHECKS + ATTENTION_BACKWARD_CHECKS + NW_CHECKS + MASK_CHECKS
+              + LOSS_CHECKS + BATCH_CHECKS)

@@ -38,7 +38,7 @@ MUTANTS = {
     "absent pairs multiplied": ("attention.py",
                                 ("out[:, d] += np.where(present[:, j], term, 0.0)",
                                  "out[:, d] += np.nan_to_num(term, nan=0.0)", 0), "fwd"),
-    "group-by joined on j": ("attention.py", ("m = row_max[ii]", "m = row_max[jj]", 0), "fwd"),
+    "group-by joined on j": ("attention.py", ("m = best[rows]", "m = best[cols]", 0), "fwd"),
     "dS sign": ("attention.py", ("ds = p * (dp - delta[:, None])", "ds = p * (dp + delta[:, None])", 0), "bwd"),
     "delta without P": ("attention.py", ("delta = np.sum(p * dp, axis=1)", "delta = np.sum(dp, axis=1)", 0), "bwd"),
     "dQ unscaled": ("attention.py", ("dq[r0:r1] = (ds @ k[:nc]) * scale", "dq[r0:r1] = (ds @ k[:nc])", 0), "bwd"),
@@ -58,13 +58,29 @@ MUTANTS = {
     "full sees only earlier blocks' keys": ("attention.py",
                                             ('return n if mask == "full" else r1', "return r1", 0),
                                             "mask"),
+    "loss without the half": ("attention.py", ("np.sum(o * o) / 2", "np.sum(o * o)", 0), "loss"),
+    "loss not squared": ("attention.py", ("np.sum(o * o) / 2", "np.sum(o) / 2", 0), "loss"),
+    "loss of |o|": ("attention.py", ("np.sum(o * o) / 2", "np.sum(np.abs(o)) / 2", 0), "loss"),
+    "forward heads shifted": ("attention.py", ("o[bi, hi] = oh", "o[bi, (hi + 1) % o.shape[1]] = oh", 0),
+                              "batch"),
+    "forward lse of another batch": ("attention.py", ("lse[bi, hi] = lh",
+                                                      "lse[(bi + 1) % lse.shape[0], hi] = lh", 0),
+                                     "batch"),
+    "backward heads shifted": ("attention.py", ("dst[bi, hi] = g", "dst[bi, (hi + 1) % dst.shape[1]] = g", 0),
+                               "batch"),
+    "backward ignores dout": ("attention.py", ("arrays = (q, k, v, np.asarray(dout, dtype=np.float64))",
+                                               "arrays = (q, k, v, np.asarray(dout, dtype=np.float64) * 0 + q)", 0),
+                              "batch_dout"),
     "bandwidth 2h^2": ("nw.py", ("/ denom", "/ (2 * denom)", 0), "nw"),
     "y against x": ("nw.py", ("(ty[r0:r1, None] - sy[None, :])", "(ty[r0:r1, None] - sx[None, :])", 0), "nw"),
     "mean of weights": ("nw.py", ("(w @ sv) / w.sum(axis=1)", "(w @ sv) / w.shape[1]", 0), "nw"),
     "min subtracted": ("nw.py", ("e.max(axis=1, keepdims=True)", "e.min(axis=1, keepdims=True)", 0), "nw"),
 }
 
-GROUPS = {"fwd": oracle_pins.ATTENTION_FORWARD_CHECKS,
+GROUPS = {"loss": oracle_pins.LOSS_CHECKS,
+          "batch": oracle_pins.BATCH_CHECKS,
+          "batch_dout": oracle_pins.BATCH_CHECKS,
+          "fwd": oracle_pins.ATTENTION_FORWARD_CHECKS,
           "bwd": oracle_pins.ATTENTION_BACKWARD_CHECKS,
           "nw": oracle_pins.NW_CHECKS,
           "mask": oracle_pins.MASK_CHECKS}
@@ -75,10 +91,10 @@ def test_mutant_is_caught(name):
     fname, edit, group = MUTANTS[name]
     mod = _load(fname, edit)
     import oracle
-    orc = types.SimpleNamespace(
-        forward_head=oracle.forward_head, forward_head_relational=oracle.forward_head_relational,
-        backward_head=oracle.backward_head, nw_average=oracle.nw_average)
-    for attr in ("forward_head", "forward_head_relational", "backward_head", "nw_average"):
+    names = ("forward_head", "forward_head_relational", "backward_head", "loss", "forward",
+             "backward", "nw_average")
+    orc = types.SimpleNamespace(**{a: getattr(oracle, a) for a in names})
+    for attr in names:
         if hasattr(mod, attr):
             setattr(orc, attr, getattr(mod, attr))
     caught = []
