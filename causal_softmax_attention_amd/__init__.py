@@ -109,10 +109,41 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _on_gpu(t, name):
+    """The public entry points run on device tensors only (no host fallback)."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
 def _bhnd(t, name):
-    if t.dim() != 4 or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError(f"{name} must be a contiguous [B, H, N, D] device tensor")
+    if t.dim() != 4 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous [B, H, N, D] tensor")
     return t.shape
+
+
+def _same(t, ref, name, what):
+    """t must be a contiguous tensor of ref's shape, dtype and device."""
+    if (tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype or t.device != ref.device
+            or not t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous tensor matching {what} in shape, "
+                         "dtype and device")
+
+
+def _lse_dtype(q):
+    import torch
+    return torch.float64 if q.dtype == torch.float64 else torch.float32
+
+
+def _check_lse(lse, q):
+    B, H, N, _ = q.shape
+    if (tuple(lse.shape) != (B, H, N) or lse.dtype != _lse_dtype(q) or lse.device != q.device
+            or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous [B, H, N] {_lse_dtype(q)} tensor on q's device")
+
+
+def _check_buffer(ws, q, name="workspace"):
+    if ws.device != q.device or not ws.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on q's device")
 
 
 def _mask_code(mask) -> int:
@@ -122,21 +153,26 @@ def _mask_code(mask) -> int:
 
 
 def _fwd_args(q, k, v, o, lse):
+    """Validate the forward's tensors (outputs included: the C side sees only
+    pointers, so a short or mistyped output would be written past its end) and
+    allocate the outputs not given."""
     import torch
     B, H, N, D = _bhnd(q, "q")
+    _dtype_code(q)
     for name, t in (("k", k), ("v", v)):
-        if _bhnd(t, name) != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError(f"{name} must match q in shape, dtype and device")
+        _same(t, q, name, "q")
     if o is None:
         o = torch.empty_like(q)
+    _same(o, q, "o", "q")
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float64 if q.dtype == torch.float64 else torch.float32,
-                          device=q.device)
+        lse = torch.empty((B, H, N), dtype=_lse_dtype(q), device=q.device)
+    _check_lse(lse, q)
     return (B, H, N, D), o, lse
 
 
 def attn_causal_fwd(q, k, v, scale: float = DEFAULT_SCALE, o=None, lse=None, stream=None):
     """Forward pass; returns (o, lse).  q, k, v: [B, H, N, 64] float64/float32/bfloat16."""
+    _on_gpu(q, "q")
     (B, H, N, D), o, lse = _fwd_args(q, k, v, o, lse)
     _check(lib().attn_causal_fwd(_dtype_code(q), B, H, N, D, float(scale), _ptr(q), _ptr(k),
                                  _ptr(v), _ptr(o), _ptr(lse), _stream(q, stream)))
@@ -147,6 +183,7 @@ def attn_fwd(q, k, v, scale: float = DEFAULT_SCALE, mask: str = "causal", window
              o=None, lse=None, stream=None):
     """Forward pass under a join predicate ("causal", "full" or "window" of
     `window` keys); returns (o, lse)."""
+    _on_gpu(q, "q")
     (B, H, N, D), o, lse = _fwd_args(q, k, v, o, lse)
     _check(lib().attn_fwd(_dtype_code(q), B, H, N, D, float(scale), _mask_code(mask), int(window),
                           _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _stream(q, stream)))
@@ -157,26 +194,34 @@ def attn_causal_bwd_workspace_bytes(dtype_code: int, B: int, H: int, N: int, D: 
     return int(lib().attn_causal_bwd_workspace_bytes(dtype_code, B, H, N, D))
 
 
-def _bwd_args(q, k, v, o, dout, dq, dk, dv, workspace):
+def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, need=None):
+    """Validate the backward's tensors (lse and the gradients included) and
+    allocate the outputs and workspace not given.  ``need`` is the workspace
+    size in bytes (the library's own figure when None)."""
     import torch
     B, H, N, D = _bhnd(q, "q")
-    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
-        if _bhnd(t, name) != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError(f"{name} must match q in shape, dtype and device")
     code = _dtype_code(q)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _same(t, q, name, "q")
+    _check_lse(lse, q)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(q) if dk is None else dk
     dv = torch.empty_like(q) if dv is None else dv
-    need = attn_causal_bwd_workspace_bytes(code, B, H, N, D)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _same(t, q, name, "q")
     if workspace is None:
+        if need is None:
+            need = attn_causal_bwd_workspace_bytes(code, B, H, N, D)
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_buffer(workspace, q)
     return (code, B, H, N, D), dq, dk, dv, workspace
 
 
 def attn_causal_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, dq=None, dk=None,
                     dv=None, workspace=None, stream=None):
     """Backward pass; returns (dq, dk, dv).  Pass dout = o for the loss sum(o^2)/2."""
-    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, dout, dq, dk, dv, workspace)
+    _on_gpu(q, "q")
+    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace)
     _check(lib().attn_causal_bwd(code, B, H, N, D, float(scale), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(q, stream)))
@@ -190,7 +235,8 @@ def attn_bwd_workspace_bytes(dtype_code: int, B: int, H: int, N: int, D: int = 6
 def attn_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, mask: str = "causal",
              window: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None):
     """Backward pass under a join predicate (as attn_fwd); returns (dq, dk, dv)."""
-    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, dout, dq, dk, dv, workspace)
+    _on_gpu(q, "q")
+    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace)
     _check(lib().attn_bwd(code, B, H, N, D, float(scale), _mask_code(mask), int(window), _ptr(q),
                           _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
@@ -198,19 +244,32 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, mask: str = "c
     return dq, dk, dv
 
 
+def _train_args(q, k, v, o, lse, workspace, loss, need=None):
+    """Validate attn_fwd_train's tensors; ``loss`` must be a one-element
+    float64 tensor on q's device (the library writes one double there)."""
+    import torch
+    shape, o, lse = _fwd_args(q, k, v, o, lse)
+    if workspace is None:
+        if need is None:
+            need = attn_bwd_workspace_bytes(_dtype_code(q), *shape)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check_buffer(workspace, q)
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float64, device=q.device)
+    if loss.numel() != 1 or loss.dtype != torch.float64 or loss.device != q.device \
+            or not loss.is_contiguous():
+        raise ValueError("loss must be a one-element float64 tensor on q's device")
+    return shape, o, lse, workspace, loss
+
+
 def attn_fwd_train(q, k, v, scale: float = DEFAULT_SCALE, mask: str = "causal", window: int = 0,
                    o=None, lse=None, workspace=None, loss=None, stream=None):
     """Forward of the training step with the loss sum(o^2)/2 fused in; returns
     (o, lse, loss, workspace): loss is a one-element float64 device tensor, and
     the workspace carries the per-row values attn_bwd_from_fwd reads."""
-    import torch
-    (B, H, N, D), o, lse = _fwd_args(q, k, v, o, lse)
+    _on_gpu(q, "q")
+    (B, H, N, D), o, lse, workspace, loss = _train_args(q, k, v, o, lse, workspace, loss)
     code = _dtype_code(q)
-    if workspace is None:
-        workspace = torch.empty(max(attn_bwd_workspace_bytes(code, B, H, N, D), 16),
-                                dtype=torch.uint8, device=q.device)
-    if loss is None:
-        loss = torch.empty(1, dtype=torch.float64, device=q.device)
     _check(lib().attn_fwd_train(code, B, H, N, D, float(scale), _mask_code(mask), int(window),
                                 _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _ptr(loss),
@@ -222,7 +281,8 @@ def attn_bwd_from_fwd(q, k, v, o, lse, workspace, scale: float = DEFAULT_SCALE,
                       mask: str = "causal", window: int = 0, dq=None, dk=None, dv=None,
                       stream=None):
     """Gradients (dq, dk, dv) of the loss sum(o^2)/2 from attn_fwd_train's outputs."""
-    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, o, dq, dk, dv, workspace)
+    _on_gpu(q, "q")
+    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, o, lse, dq, dk, dv, workspace)
     _check(lib().attn_bwd_from_fwd(code, B, H, N, D, float(scale), _mask_code(mask), int(window),
                                    _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dq),
                                    _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(),
@@ -236,10 +296,13 @@ def nw_gauss_average(tx, ty, sx, sy, sv, denom: float = 0.25, out=None, stream=N
     for name, t in (("tx", tx), ("ty", ty), ("sx", sx), ("sy", sy), ("sv", sv)):
         if t.dim() != 1 or t.dtype != torch.float32 or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous 1-D float32 device tensor")
+        if t.device != tx.device:
+            raise ValueError(f"{name} must be on tx's device")
     if ty.shape != tx.shape or sy.shape != sx.shape or sv.shape != sx.shape:
         raise ValueError("target columns and source columns must have matching lengths")
     if out is None:
         out = torch.empty_like(tx)
+    _same(out, tx, "out", "tx")
     _check(lib().nw_gauss_average(tx.numel(), _ptr(tx), _ptr(ty), sx.numel(), _ptr(sx),
                                   _ptr(sy), _ptr(sv), float(denom), _ptr(out),
                                   _stream(tx, stream)))
@@ -259,6 +322,11 @@ def attn_matrix_to_table(m, t=None, d=None, x=None, stream=None):
     t = torch.empty(T * D, dtype=torch.int64, device=m.device) if t is None else t
     d = torch.empty(T * D, dtype=torch.int64, device=m.device) if d is None else d
     x = torch.empty(T * D, dtype=m.dtype, device=m.device) if x is None else x
+    for name, c, dt in (("t", t, torch.int64), ("d", d, torch.int64), ("x", x, m.dtype)):
+        if (c.dim() != 1 or c.numel() != T * D or c.dtype != dt or c.device != m.device
+                or not c.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous 1-D {dt} tensor of T * D elements "
+                             "on m's device")
     _check(lib().attn_matrix_to_table(_dtype_code(m), T, D, _ptr(m), _ptr(t), _ptr(d), _ptr(x),
                                       _stream(m, stream)))
     return t, d, x
@@ -282,12 +350,20 @@ def attn_table_to_matrix(t, d, x, T: int, D: int, m=None, workspace=None, status
         raise ValueError("t and d must be int64")
     if not (t.numel() == d.numel() == x.numel()):
         raise ValueError("t, d and x must have one length")
+    if t.device != x.device or d.device != x.device:
+        raise ValueError("t, d and x must be on one device")
     m = torch.empty((T, D), dtype=x.dtype, device=x.device) if m is None else m
+    if (tuple(m.shape) != (T, D) or m.dtype != x.dtype or m.device != x.device
+            or not m.is_contiguous()):
+        raise ValueError("m must be a contiguous [T, D] tensor of x's dtype on x's device")
     need = attn_table_workspace_bytes(T, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check_buffer(workspace, x)
     if status is None:
         status = torch.empty(1, dtype=torch.int32, device=x.device)
+    if status.numel() != 1 or status.dtype != torch.int32 or status.device != x.device:
+        raise ValueError("status must be a one-element int32 tensor on x's device")
     _check(lib().attn_table_to_matrix(_dtype_code(x), t.numel(), _ptr(t), _ptr(d), _ptr(x), T, D,
                                       _ptr(m), _ptr(status), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(),
@@ -312,8 +388,16 @@ def attn_qkv_project(x, wq, wk, wv, heads: int, q=None, k=None, v=None, stream=N
         _dev(w, name, 2)
         if tuple(w.shape) != (Dm, heads * 64) or w.dtype != x.dtype:
             raise ValueError(f"{name} must be [{Dm}, {heads * 64}] of x's dtype")
+    for name, w in (("wq", wq), ("wk", wk), ("wv", wv)):
+        if w.device != x.device:
+            raise ValueError(f"{name} must be on x's device")
     outs = [torch.empty((B, heads, N, 64), dtype=x.dtype, device=x.device) if o is None else o
             for o in (q, k, v)]
+    for name, o in zip("qkv", outs):
+        if (tuple(o.shape) != (B, heads, N, 64) or o.dtype != x.dtype or o.device != x.device
+                or not o.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous [B, heads, N, 64] tensor of x's "
+                             "dtype on x's device")
     _check(lib().attn_qkv_project(_dtype_code(x), B, N, Dm, heads, _ptr(x), _ptr(wq), _ptr(wk),
                                   _ptr(wv), *(_ptr(o) for o in outs), _stream(x, stream)))
     return tuple(outs)

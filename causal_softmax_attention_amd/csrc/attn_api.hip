@@ -45,6 +45,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 // element count must fit the int/int64 arithmetic used on the device.
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxHeads = int64_t(1) << 24;
+constexpr int64_t kMaxGroups = int64_t(1) << 24;  // x 256 threads = 2^32 work-items
 // Largest element count of a matrix, table or weight the adapter and the
 // projections index (int64 offsets; 2^40 elements is far beyond one GPU).
 constexpr int64_t kMaxCells = int64_t(1) << 40;
@@ -59,6 +60,14 @@ int check_sizes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double sc
   if (N > kMaxN) return fail(ATTN_EINVAL, "N=%lld exceeds %lld", (long long)N, (long long)kMaxN);
   if (B > kMaxHeads / H)
     return fail(ATTN_EINVAL, "B*H exceeds %lld", (long long)kMaxHeads);
+  // Every launch over heads x row blocks takes at least 32 rows per 256-thread
+  // workgroup, with heads padded to a multiple of 8; a launch's work-items
+  // (workgroups x 256) must stay below 2^32.
+  const int64_t padded = (B * H + 7) / 8 * 8, blocks = (N + 31) / 32;
+  if (padded * blocks >= kMaxGroups)
+    return fail(ATTN_EINVAL, "B*H=%lld heads of N=%lld need %lld workgroups of 32 rows; the limit is %lld",
+                (long long)(B * H), (long long)N, (long long)(padded * blocks),
+                (long long)kMaxGroups - 1);
   if (!(scale > 0.0) || !isfinite(scale)) return fail(ATTN_EINVAL, "scale must be finite and > 0");
   return ATTN_OK;
 }
@@ -196,29 +205,29 @@ int bwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
 
 extern "C" {
 
-int attn_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+int attn_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, attn_mask_t mask,
              int64_t window, const void* q, const void* k, const void* v, void* o, void* lse,
              void* stream) {
   return fwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, lse, nullptr,
                   (hipStream_t)stream);
 }
 
-int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+int attn_causal_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
                     const void* q, const void* k, const void* v, void* o, void* lse,
                     void* stream) {
   return attn_fwd(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, q, k, v, o, lse, stream);
 }
 
-size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
+size_t attn_causal_bwd_workspace_bytes(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
   if (check_sizes(dtype, B, H, N, D, 1.0) != ATTN_OK) return 0;
   return workspace_bytes_for(dtype, B * H, N);
 }
 
-size_t attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
+size_t attn_bwd_workspace_bytes(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D) {
   return attn_causal_bwd_workspace_bytes(dtype, B, H, N, D);
 }
 
-int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+int attn_bwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, attn_mask_t mask,
              int64_t window, const void* q, const void* k, const void* v, const void* o,
              const void* dout, const void* lse, void* dq, void* dk, void* dv, void* workspace,
              size_t workspace_bytes, void* stream) {
@@ -226,7 +235,7 @@ int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
                   workspace, workspace_bytes, false, (hipStream_t)stream);
 }
 
-int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+int attn_causal_bwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
                     const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const void* lse, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream) {
@@ -234,7 +243,7 @@ int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, doubl
                   dv, workspace, workspace_bytes, stream);
 }
 
-int attn_fwd_train(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
+int attn_fwd_train(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, attn_mask_t mask,
                    int64_t window, const void* q, const void* k, const void* v, void* o,
                    void* lse, void* workspace, size_t workspace_bytes, double* loss,
                    void* stream) {
@@ -263,8 +272,8 @@ int attn_fwd_train(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double
                     "attn_fwd_train loss launch");
 }
 
-int attn_bwd_from_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                      int mask, int64_t window, const void* q, const void* k, const void* v,
+int attn_bwd_from_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                      attn_mask_t mask, int64_t window, const void* q, const void* k, const void* v,
                       const void* o, const void* lse, void* dq, void* dk, void* dv,
                       void* workspace, size_t workspace_bytes, void* stream) {
   return bwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, o, lse, dq, dk, dv,
@@ -297,7 +306,7 @@ size_t attn_table_workspace_bytes(int64_t T, int64_t D) {
   return attn::table_workspace_bytes(T, D);
 }
 
-int attn_table_to_matrix(int dtype, int64_t rows, const int64_t* t, const int64_t* d,
+int attn_table_to_matrix(attn_dtype_t dtype, int64_t rows, const int64_t* t, const int64_t* d,
                          const void* x, int64_t T, int64_t D, void* m, int32_t* status,
                          void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16)
@@ -329,7 +338,7 @@ int attn_table_to_matrix(int dtype, int64_t rows, const int64_t* t, const int64_
                     "attn_table_to_matrix launch");
 }
 
-int attn_matrix_to_table(int dtype, int64_t T, int64_t D, const void* m, int64_t* t, int64_t* d,
+int attn_matrix_to_table(attn_dtype_t dtype, int64_t T, int64_t D, const void* m, int64_t* t, int64_t* d,
                          void* x, void* stream) {
   if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16)
     return fail(ATTN_EINVAL, "unknown dtype %d", dtype);
@@ -347,7 +356,7 @@ int attn_matrix_to_table(int dtype, int64_t T, int64_t D, const void* m, int64_t
                     "attn_matrix_to_table launch");
 }
 
-int attn_qkv_project(int dtype, int64_t B, int64_t N, int64_t Dm, int64_t H, const void* x,
+int attn_qkv_project(attn_dtype_t dtype, int64_t B, int64_t N, int64_t Dm, int64_t H, const void* x,
                      const void* wq, const void* wk, const void* wv, void* q, void* k, void* v,
                      void* stream) {
   if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16)

@@ -29,6 +29,9 @@
  *     message.  The library keeps no other state; calls from several host
  *     threads are safe.
  *   - Outputs must not alias inputs, except dout == o in the backward passes.
+ *   - Size limits of the attention entry points (ATTN_EINVAL beyond them):
+ *     N <= 2^24, B*H <= 2^24, and (B*H rounded up to a multiple of 8) *
+ *     ceil(N / 32) < 2^24, so that no launch exceeds 2^32 work-items.
  */
 #ifndef ATTN_H
 #define ATTN_H
@@ -77,7 +80,7 @@ typedef enum { ATTN_MASK_CAUSAL = 0, ATTN_MASK_FULL = 1, ATTN_MASK_WINDOW = 2 } 
  *   scale  multiplier of q.k, finite and > 0 (the pages use 1/8 = 1/sqrt(64))
  *   q, k, v  inputs [B, H, N, D];  o output [B, H, N, D];  lse output [B, H, N]
  * Returns ATTN_OK / ATTN_EINVAL / ATTN_EUNSUPPORTED / ATTN_EHIP. */
-ATTN_API int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+ATTN_API int attn_causal_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
                     const void* q, const void* k, const void* v, void* o, void* lse,
                     void* stream);
 
@@ -88,14 +91,17 @@ ATTN_API int attn_causal_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t
  * attn_causal_fwd(...) is attn_fwd(..., ATTN_MASK_CAUSAL, 0, ...).
  * Returns ATTN_OK / ATTN_EINVAL (also for an unknown mask or window < 1) /
  * ATTN_EUNSUPPORTED / ATTN_EHIP. */
-ATTN_API int attn_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                      int mask, int64_t window, const void* q, const void* k, const void* v,
+ATTN_API int attn_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                      attn_mask_t mask, int64_t window, const void* q, const void* k, const void* v,
                       void* o, void* lse, void* stream);
 
-/* Bytes of device workspace attn_causal_bwd needs for these sizes (0 on an
- * invalid request).  The caller allocates it; its contents need not be
- * initialised and are garbage afterwards. */
-ATTN_API size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D);
+/* Bytes of device workspace attn_causal_bwd needs for these sizes.  On a
+ * request attn_causal_bwd would reject (bad dtype or sizes) it returns 0 and
+ * sets attn_last_error(); a caller that then passes a 0-byte workspace gets
+ * ATTN_EINVAL from attn_causal_bwd, before any launch.  The caller allocates
+ * the workspace; its contents need not be initialised and are garbage
+ * afterwards. */
+ATTN_API size_t attn_causal_bwd_workspace_bytes(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D);
 
 /* Backward pass: dq, dk, dv of a loss with upstream gradient dout (the pages'
  * GRADIENT statement: grad(loss, q.x), grad(loss, k.x), grad(loss, v.x) of
@@ -106,22 +112,22 @@ ATTN_API size_t attn_causal_bwd_workspace_bytes(int dtype, int64_t B, int64_t H,
  *   dq, dk, dv  outputs [B, H, N, D] in dtype
  *   workspace   device memory of at least attn_causal_bwd_workspace_bytes()
  * Returns ATTN_OK / ATTN_EINVAL / ATTN_EUNSUPPORTED / ATTN_EHIP. */
-ATTN_API int attn_causal_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+ATTN_API int attn_causal_bwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
                     const void* q, const void* k, const void* v, const void* o,
                     const void* dout, const void* lse, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes for attn_bwd (the same for every mask; equal to
  * attn_causal_bwd_workspace_bytes). */
-ATTN_API size_t attn_bwd_workspace_bytes(int dtype, int64_t B, int64_t H, int64_t N, int64_t D);
+ATTN_API size_t attn_bwd_workspace_bytes(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D);
 
 /* The backward pass under any join predicate: as attn_causal_bwd, with mask
  * and window as in attn_fwd; lse must come from attn_fwd with the same mask
  * and window.  attn_causal_bwd(...) is attn_bwd(..., ATTN_MASK_CAUSAL, 0, ...).
  * Returns ATTN_OK / ATTN_EINVAL (also for an unknown mask or window < 1) /
  * ATTN_EUNSUPPORTED / ATTN_EHIP. */
-ATTN_API int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                      int mask, int64_t window, const void* q, const void* k, const void* v,
+ATTN_API int attn_bwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                      attn_mask_t mask, int64_t window, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const void* lse, void* dq, void* dk,
                       void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -137,12 +143,12 @@ ATTN_API int attn_bwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, dou
  * instead of recomputing them (one kernel fewer).  Pass it the same sizes,
  * scale, mask, window, q, k, v, o, lse and workspace, unchanged in between.
  * Returns ATTN_OK / ATTN_EINVAL / ATTN_EUNSUPPORTED / ATTN_EHIP. */
-ATTN_API int attn_fwd_train(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                            int mask, int64_t window, const void* q, const void* k,
+ATTN_API int attn_fwd_train(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                            attn_mask_t mask, int64_t window, const void* q, const void* k,
                             const void* v, void* o, void* lse, void* workspace,
                             size_t workspace_bytes, double* loss, void* stream);
-ATTN_API int attn_bwd_from_fwd(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
-                               int mask, int64_t window, const void* q, const void* k,
+ATTN_API int attn_bwd_from_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                               attn_mask_t mask, int64_t window, const void* q, const void* k,
                                const void* v, const void* o, const void* lse, void* dq, void* dk,
                                void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
@@ -183,10 +189,10 @@ ATTN_API int nw_gauss_average(int64_t n_targets, const float* tx, const float* t
  *   status 4 bytes.  m, the workspace and status must not overlap the inputs
  *   or each other.  At most 2^40 rows and 2^40 cells (ATTN_EINVAL).
  *   attn_table_workspace_bytes returns 0 for sizes the call would reject. */
-ATTN_API int attn_matrix_to_table(int dtype, int64_t T, int64_t D, const void* m, int64_t* t,
+ATTN_API int attn_matrix_to_table(attn_dtype_t dtype, int64_t T, int64_t D, const void* m, int64_t* t,
                                   int64_t* d, void* x, void* stream);
 ATTN_API size_t attn_table_workspace_bytes(int64_t T, int64_t D);
-ATTN_API int attn_table_to_matrix(int dtype, int64_t rows, const int64_t* t, const int64_t* d,
+ATTN_API int attn_table_to_matrix(attn_dtype_t dtype, int64_t rows, const int64_t* t, const int64_t* d,
                                   const void* x, int64_t T, int64_t D, void* m, int32_t* status,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
@@ -202,7 +208,7 @@ ATTN_API int attn_table_to_matrix(int dtype, int64_t rows, const int64_t* t, con
  * All pointers 16-byte aligned; the outputs must not overlap each other or
  * the inputs.  Limits (ATTN_EINVAL): sizes >= 1, H <= 65535, B*N < 2^31,
  * N <= 2^24, x and each weight at most 2^40 elements. */
-ATTN_API int attn_qkv_project(int dtype, int64_t B, int64_t N, int64_t Dm, int64_t H,
+ATTN_API int attn_qkv_project(attn_dtype_t dtype, int64_t B, int64_t N, int64_t Dm, int64_t H,
                               const void* x, const void* wq, const void* wk, const void* wv,
                               void* q, void* k, void* v, void* stream);
 
@@ -230,7 +236,11 @@ enum {
 ATTN_API int attn_set_kernel_timer(int slot, void* start, void* stop);
 
 /* Message of the calling thread's most recent error ("" if none).  The pointer
- * stays valid until that thread's next call into the library. */
+ * stays valid until that thread's next call into the library.  This mirrors
+ * how the demo script of "Show HN: automatic deduction of FlashAttention
+ * kernel from 25 lines of SQL" treats a failing engine (its report.attempt
+ * helper records the failure and the run goes on): every entry point returns
+ * a code instead of aborting, and the message says what failed. */
 ATTN_API const char* attn_last_error(void);
 
 #ifdef __cplusplus

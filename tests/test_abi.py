@@ -286,3 +286,112 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         csa.lib()
     with pytest.raises(RuntimeError, match="is missing"):
         csa.attn_table_workspace_bytes(4, 4)
+
+
+@pytest.mark.parametrize("B,H,N,ok", [
+    (1 << 14, 1 << 10, 128, False),   # 2^24 heads of 128 tokens: 2^26 workgroups of 32 rows
+    (1 << 12, 1 << 10, 512, False),   # 2^22 heads x 16 blocks = 2^26
+    (1 << 11, 1 << 10, 256, False),   # 2^21 heads x 8 blocks = 2^24 (the first size refused)
+    (1 << 11, 1 << 10, 224, True),    # 2^21 heads x 7 blocks < 2^24
+    (1, 1, 1 << 24, True),            # the longest head: 2^19 blocks
+])
+def test_grid_limit(L, B, H, N, ok):
+    """A launch over heads x 32-row blocks must stay below 2^32 work-items: the
+    size check refuses it (ATTN_EINVAL) instead of the launch failing.  The
+    accepted sizes are checked through the workspace query, which runs the
+    same size check and launches nothing."""
+    if ok:
+        assert L.attn_causal_bwd_workspace_bytes(2, B, H, N, 64) > 0, csa.attn_last_error()
+    else:
+        # refused by the size check, before the dummy pointers are looked at
+        assert fwd(L, B=B, H=H, N=N) == csa.ATTN_EINVAL
+        assert "workgroups" in csa.attn_last_error()
+        assert L.attn_causal_bwd_workspace_bytes(2, B, H, N, 64) == 0
+
+
+# ---- the binding validates every tensor, outputs included (the C side sees
+# only pointers, so a short or mistyped output would be written past its end)
+
+import torch  # noqa: E402
+
+
+def _qkv(dtype=torch.bfloat16, shape=(1, 2, 5, 64)):
+    return [torch.zeros(shape, dtype=dtype) for _ in range(3)]
+
+
+def test_binding_requires_device_tensors():
+    q, k, v = _qkv()
+    with pytest.raises(ValueError, match="device tensor"):
+        csa.attn_causal_fwd(q, k, v)
+    with pytest.raises(ValueError, match="device tensor"):
+        csa.attn_causal_bwd(q, k, v, q, q, torch.zeros(1, 2, 5))
+
+
+@pytest.mark.parametrize("dtype,lse_dtype", [(torch.bfloat16, torch.float32),
+                                              (torch.float32, torch.float32),
+                                              (torch.float64, torch.float64)])
+def test_binding_accepts_matching_outputs(dtype, lse_dtype):
+    q, k, v = _qkv(dtype)
+    shape, o, lse = csa._fwd_args(q, k, v, torch.empty_like(q), torch.empty(1, 2, 5, dtype=lse_dtype))
+    assert tuple(shape) == (1, 2, 5, 64)
+    csa._bwd_args(q, k, v, o, o, lse, torch.empty_like(q), torch.empty_like(q),
+                  torch.empty_like(q), torch.empty(64, dtype=torch.uint8))
+    csa._train_args(q, k, v, o, lse, torch.empty(64, dtype=torch.uint8),
+                    torch.empty(1, dtype=torch.float64))
+
+
+@pytest.mark.parametrize("case", ["o short", "o dtype", "o strided", "lse dtype f64 path",
+                                  "lse short", "lse float64 for bf16", "lse strided"])
+def test_binding_rejects_bad_forward_outputs(case):
+    dtype = torch.float64 if "f64 path" in case else torch.bfloat16
+    q, k, v = _qkv(dtype)
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 2, 5, dtype=torch.float64 if dtype == torch.float64 else torch.float32)
+    if case == "o short":
+        o = torch.empty(1, 2, 4, 64, dtype=dtype)
+    elif case == "o dtype":
+        o = torch.empty(1, 2, 5, 64, dtype=torch.float32)
+    elif case == "o strided":
+        o = torch.empty(1, 2, 64, 5, dtype=dtype).transpose(2, 3)
+    elif case == "lse dtype f64 path":
+        lse = torch.empty(1, 2, 5, dtype=torch.float32)
+    elif case == "lse short":
+        lse = torch.empty(1, 2, 4)
+    elif case == "lse float64 for bf16":
+        lse = torch.empty(1, 2, 5, dtype=torch.float64)
+    elif case == "lse strided":
+        lse = torch.empty(1, 5, 2).transpose(1, 2)
+    with pytest.raises(ValueError):
+        csa._fwd_args(q, k, v, o, lse)
+
+
+@pytest.mark.parametrize("case", ["dq short", "dk dtype", "dv strided", "lse short", "lse dtype",
+                                  "dout shape"])
+def test_binding_rejects_bad_backward_tensors(case):
+    q, k, v = _qkv()
+    o, dout = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty(1, 2, 5)
+    g = {n: torch.empty_like(q) for n in ("dq", "dk", "dv")}
+    if case == "dq short":
+        g["dq"] = torch.empty(1, 2, 5, 32, dtype=q.dtype)
+    elif case == "dk dtype":
+        g["dk"] = torch.empty(1, 2, 5, 64, dtype=torch.float32)
+    elif case == "dv strided":
+        g["dv"] = torch.empty(1, 2, 64, 5, dtype=q.dtype).transpose(2, 3)
+    elif case == "lse short":
+        lse = torch.empty(1, 2, 3)
+    elif case == "lse dtype":
+        lse = torch.empty(1, 2, 5, dtype=torch.float64)
+    elif case == "dout shape":
+        dout = torch.empty(1, 2, 6, 64, dtype=q.dtype)
+    with pytest.raises(ValueError):
+        csa._bwd_args(q, k, v, o, dout, lse, g["dq"], g["dk"], g["dv"],
+                      torch.empty(64, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("loss", [torch.empty(1, dtype=torch.float32), torch.empty(2, dtype=torch.float64),
+                                  torch.empty(0, dtype=torch.float64)])
+def test_binding_rejects_bad_loss(loss):
+    q, k, v = _qkv()
+    with pytest.raises(ValueError, match="loss"):
+        csa._train_args(q, k, v, None, None, torch.empty(64, dtype=torch.uint8), loss)
