@@ -40,10 +40,13 @@ HBM_PEAK = 8000.0        # GB/s
 D = 64
 METRIC = "causal attn fwd+bwd TFLOP/s at N=4096 D=64 bf16; % of MFMA peak"
 
-# Algorithmic flops per pair (i, j <= i) of each timed kernel: the products its
-# outputs need from its inputs.  fwd: S = Q K^T and O = P V; dK/dV pass:
-# S, dP = dO V^T, dV = P^T dO, dK = dS^T Q; dQ pass: S, dP, dQ = dS K.
-KERNEL_FLOPS_PER_PAIR = {"fwd": 4 * D, "bwd_dkdv": 8 * D, "bwd_dq": 6 * D, "bwd_pre": 0}
+# Algorithmic flops per pair (i, j <= i) credited to each timed kernel: the
+# method's five backward products are S, dP = dO V^T, dV = P^T dO, dK = dS^T Q
+# and dQ = dS K (10 D), the forward's two S and P V (4 D).  The dK/dV pass
+# forms the first four; the dQ pass is credited with dQ alone (2 D): its own
+# recomputation of S and dP is work the method does not need.  The credits sum
+# to the 14 D of the headline.
+KERNEL_FLOPS_PER_PAIR = {"fwd": 4 * D, "bwd_dkdv": 8 * D, "bwd_dq": 2 * D, "bwd_pre": 0}
 COPY_BYTES = 256 << 20   # the plain device copy used to calibrate HBM byte counters
 
 
@@ -96,7 +99,8 @@ def make_inputs(name):
 
 def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask="causal",
                    window=0, fused=False):
-    """Run `steps` timed steps; returns (ms_per_step, {slot: mean ms}, outputs).
+    """Run `steps` timed steps; returns (mean ms per step, wall ms per step,
+    {slot: mean ms}, outputs, sorted per-step ms).
     The causal predicate goes through attn_causal_fwd / _bwd, others through
     attn_fwd / attn_bwd; fused: attn_fwd_train (forward + loss + the
     backward's per-row values) and attn_bwd_from_fwd."""
@@ -146,6 +150,7 @@ def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask=
             events.append(ev)
         torch.cuda.synchronize()
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
@@ -153,44 +158,142 @@ def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask=
         if per_kernel:
             for s in slots:
                 csa.attn_set_kernel_timer(s, *events[i][s])
+        marks[i].record()
         step()
+    marks[steps].record()
     stop.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     for s in slots:
         csa.attn_set_kernel_timer(s, None, None)
     ms = start.elapsed_time(stop) / steps
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(steps))
     per = {}
     if per_kernel:
         for s in slots:
             per[csa.TIMER_NAMES[s]] = sum(e[s][0].elapsed_time(e[s][1]) for e in events) / steps
-    return ms, wall, per, (o, lse)
+    return ms, wall, per, (o, lse), per_step
+
+
+def _blas_vendor() -> str:
+    import numpy as np
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:  # noqa: BLE001
+        return "unknown"
 
 
 def cpu_baseline(a, budget_s=10.0):
-    """The oracle on whole heads of the workload until ~budget_s of CPU work."""
+    """The oracle (as it stands) on whole heads of the workload until ~budget_s
+    of wall time: its [B, H, N, D] wrappers with their thread pool over heads,
+    one worker per core of this process's CPU share, one BLAS thread each."""
+    import numpy as np
+
+    import causal_softmax_attention_amd.inputs as inp
     import oracle
+    cores = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS")
+    if share and share.isdigit() and int(share) > 0:
+        cores = min(cores, int(share))
+    import contextlib
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i["num_threads"] for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=1)
     except Exception:  # noqa: BLE001
-        threads = 1
+        limit = contextlib.nullcontext()
     B, H, N = a.q.shape[:3]
+    flat = [(b, h) for b in range(B) for h in range(H)]
     done, t0 = 0, time.perf_counter()
-    order = [(b, h) for b in range(B) for h in range(H)]
-    while done < len(order):
-        b, h = order[done]
-        q, k, v = (a.as_f64(x)[b, h] for x in "qkv")
-        oracle.forward_head(q, k, v, 0.125)
-        oracle.backward_head(q, k, v, None, 0.125)
-        done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
+    with limit:
+        while done < len(flat):
+            batch = flat[done:done + cores]
+            def f64(name):
+                x = getattr(a, name)
+                sel = np.stack([x[b, h] for b, h in batch])[None]
+                return inp.bf16_bits_to_f32(sel).astype(np.float64)
+            q, k, v = f64("q"), f64("k"), f64("v")
+            oracle.forward(q, k, v, 0.125, workers=cores)
+            oracle.backward(q, k, v, None, 0.125, workers=cores)
+            done += len(batch)
+            if time.perf_counter() - t0 >= budget_s:
+                break
     el = time.perf_counter() - t0
     flops = 14 * D * pairs(done, N)
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} of {B * H} heads (N={N}), float64 fwd + bwd, {el:.1f} s wall; "
-                      f"BLAS threads={threads}, elementwise numpy single-threaded"}
+                      f"a pool of {cores} threads over heads (os.sched_getaffinity within the "
+                      f"process's OMP_NUM_THREADS share), 1 BLAS thread each",
+            "blas": _blas_vendor()}
+
+
+class SclkSampler:
+    """Samples the GPU's graphics clock (MHz) from a background thread while
+    the timed region runs, through the amdsmi Python module: the current GFX
+    clock (amdsmi_get_clock_info) and, where the GPU metrics table has them,
+    the per-XCD current gfx clocks.  The first raw reading is kept, so the
+    record shows which fields the clock came from."""
+
+    def __init__(self, period_s=0.002):
+        import threading
+        self.samples, self.xcd_samples, self.error, self.raw = [], [], None, {}
+        self._stop = threading.Event()
+        self._period = period_s
+        self._ok = False
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._amdsmi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+            c = amdsmi.amdsmi_get_clock_info(self._h, amdsmi.AmdSmiClkType.GFX)
+            self.raw["clock_info_gfx"] = {k: c[k] for k in c}
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+                self.raw["gpu_metrics"] = {k: m[k] for k in m
+                                           if "gfxclk" in k or "clk" in k.lower()}
+            except Exception as e:  # noqa: BLE001
+                self.raw["gpu_metrics"] = str(e)
+            self._ok = True
+        except Exception as e:  # noqa: BLE001
+            self.error = f"amdsmi: {e}"
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        am, h = self._amdsmi, self._h
+        while not self._stop.is_set():
+            try:
+                c = am.amdsmi_get_clock_info(h, am.AmdSmiClkType.GFX)
+                self.samples.append(float(c["clk"]))
+                m = am.amdsmi_get_gpu_metrics_info(h)
+                xs = m.get("current_gfxclks")
+                if isinstance(xs, (list, tuple)):
+                    xs = [x for x in xs if isinstance(x, (int, float)) and 0 < x < 10000]
+                    if xs:
+                        self.xcd_samples.append(sum(xs) / len(xs))
+            except Exception as e:  # noqa: BLE001
+                self.error = str(e)
+                return
+            self._stop.wait(self._period)
+
+    def __enter__(self):
+        if self._ok:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        def stats(v):
+            if not v:
+                return None
+            v = sorted(v)
+            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v)}
+        return {"gfx_clock_info_mhz": stats(self.samples),
+                "gpu_metrics_current_gfxclks_mean_mhz": stats(self.xcd_samples),
+                "raw_first_reading": self.raw, "error": self.error}
 
 
 def secondary(steps):
@@ -203,13 +306,13 @@ def secondary(steps):
     import causal_softmax_attention_amd.inputs as inp
     out = {}
     a, (q, k, v), _ = make_inputs("fp32_2k")
-    ms, _, per, _ = time_attention(q, k, v, steps, 2, with_bwd=False)
+    ms, _, per, _, _ = time_attention(q, k, v, steps, 2, with_bwd=False)
     fl = 4 * D * pairs(64, 2048)
     out["fp32_2k_fwd"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
                           "frac_of_fp32_mfma_peak": fl / ms / 1e9 / F32_PEAK}
     del q, k, v
     a, (q, k, v), _ = make_inputs("bf16_32k")
-    ms, _, per, _ = time_attention(q, k, v, max(2, steps // 4), 1)
+    ms, _, per, _, _ = time_attention(q, k, v, max(2, steps // 4), 1)
     fl = 14 * D * pairs(16, 32768)
     out["bf16_32k_fwd_bwd"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
                                "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
@@ -218,7 +321,7 @@ def secondary(steps):
     # the same step with the loss fused into the forward (attn_fwd_train +
     # attn_bwd_from_fwd): the backward's per-row pass is folded away
     a, (q, k, v), _ = make_inputs("bf16_4k")
-    ms, _, per, _ = time_attention(q, k, v, steps, 2, fused=True)
+    ms, _, per, _, _ = time_attention(q, k, v, steps, 2, fused=True)
     fl = 14 * D * pairs(256, 4096)
     out["bf16_4k_train_step_fused_loss"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
                                             "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
@@ -230,7 +333,7 @@ def secondary(steps):
     B_, H_, N_ = q.shape[:3]
     for mask, window, key in (("full", 0, "bf16_4k_full_fwd_bwd"),
                               ("window", 512, "bf16_4k_window512_fwd_bwd")):
-        ms, _, per, _ = time_attention(q, k, v, max(2, steps // 2), 1, mask=mask, window=window)
+        ms, _, per, _, _ = time_attention(q, k, v, max(2, steps // 2), 1, mask=mask, window=window)
         npairs = B_ * H_ * (N_ * N_ if mask == "full" else
                             sum(min(i + 1, window) for i in range(N_)))
         fl = 14 * D * npairs
@@ -238,7 +341,7 @@ def secondary(steps):
                     "pairs": npairs, "kernels_ms": per}
     del q, k, v
     a, (q, k, v), _ = make_inputs("fp64_256")
-    ms, _, per, _ = time_attention(q, k, v, steps, 2)
+    ms, _, per, _, _ = time_attention(q, k, v, steps, 2)
     out["fp64_256_fwd_bwd"] = {"us": ms * 1e3, "kernels_us": {k_: v_ * 1e3 for k_, v_ in per.items()}}
     nw = inp.nw_inputs()
     cols = [torch.from_numpy(x).to("cuda:0") for x in (nw.tx, nw.ty, nw.sx, nw.sy, nw.sv)]
@@ -376,7 +479,8 @@ def main():
     a, (q, k, v), _ = make_inputs("bf16_4k")
     B, H, N = q.shape[:3]
     log(f"timing {args.steps} steps after {args.warmup} warmup")
-    ms, wall, per, _ = time_attention(q, k, v, args.steps, args.warmup)
+    with SclkSampler() as clk:
+        ms, wall, per, _, per_step = time_attention(q, k, v, args.steps, args.warmup)
     flops = 14 * D * pairs(B * H, N)
     value = flops / ms / 1e9
     # dominant kernel
@@ -398,6 +502,10 @@ def main():
                    "head_dim": D, "parallelism": "none (1 GPU)"},
         "frac_of_bf16_mfma_peak": round(value / BF16_PEAK, 4),
         "wall_ms_per_step": round(wall, 4),
+        "ms_per_step_median": round(per_step[len(per_step) // 2], 4),
+        "ms_per_step_min": round(per_step[0], 4),
+        "TFLOP/s_at_median": round(flops / per_step[len(per_step) // 2] / 1e9, 2),
+        "sclk_mhz": clk.summary(),
         "kernels_ms": {k_: round(v_, 4) for k_, v_ in per.items()},
         "roofline": roof,
     }

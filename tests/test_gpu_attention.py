@@ -42,25 +42,69 @@ def _heads(a: inp.AttentionInputs, sel=None):
     return sel, [(q[b, h], k[b, h], v[b, h]) for b, h in sel]
 
 
+def _stacked(a, sel):
+    """The selected heads as float64 arrays [1, len(sel), N, D] (q, k, v), for the
+    oracle's batched functions and their thread pool over heads."""
+    sel, heads = _heads(a, sel)
+    return sel, [np.stack([hd[i] for hd in heads])[None] for i in range(3)]
+
+
+WORKERS = 8
+
+
 def _check_fwd(a, o, lse, sel=None, tol=None):
     tol = tol or TOL[a.dtype]
-    sel, heads = _heads(a, sel)
+    sel, (q, k, v) = _stacked(a, sel)
     oh, lh = to_host(o), to_host(lse)
-    for (b, h), (q, k, v) in zip(sel, heads):
-        wo, wl = oracle.forward_head(q, k, v, S)[:2]
-        assert_close(f"o[{b},{h}]", oh[b, h], wo, tol)
-        assert_close(f"lse[{b},{h}]", lh[b, h], wl, tol)
+    wo, wl = oracle.forward(q, k, v, S, workers=WORKERS)
+    for n, (b, h) in enumerate(sel):
+        assert_close(f"o[{b},{h}]", oh[b, h], wo[0, n], tol)
+        assert_close(f"lse[{b},{h}]", lh[b, h], wl[0, n], tol)
 
 
 def _check_bwd(a, grads, sel=None, dout=None):
     tol = TOL[a.dtype]
-    sel, heads = _heads(a, sel)
+    sel, (q, k, v) = _stacked(a, sel)
     gh = [to_host(g) for g in grads]
-    for (b, h), (q, k, v) in zip(sel, heads):
-        d = None if dout is None else dout[b, h]
-        want = oracle.backward_head(q, k, v, d, S)
+    d = None if dout is None else np.stack([dout[b, h] for b, h in sel])[None]
+    want = oracle.backward(q, k, v, d, S, workers=WORKERS)
+    for n, (b, h) in enumerate(sel):
         for name, g, w in zip(("dq", "dk", "dv"), gh, want):
-            assert_close(f"{name}[{b},{h}]", g[b, h], w, tol)
+            assert_close(f"{name}[{b},{h}]", g[b, h], w[0, n], tol)
+
+
+def _check_all_heads(a, o, lse, grads, tol):
+    """Per-head properties that hold at any size, on every head of a full-size
+    run (computed on the device): every output finite; row 0 of o equals V[0]
+    (its only pair); the rows of P sum to 1, so sum_j dV_j = sum_i dO_i (dO = o);
+    each row of dS sums to 0, so sum_j dK_j = 0 up to rounding."""
+    v = to_dev(a.v, a.dtype)
+    for name, t in (("o", o), ("lse", lse)) + tuple(zip(("dq", "dk", "dv"), grads)):
+        assert bool(torch.isfinite(t).all()), f"{name} has a non-finite entry"
+    o64, v64 = o.double(), v.double()
+    B, H = o.shape[:2]
+    e0 = ((o64[:, :, 0] - v64[:, :, 0]).abs().amax(dim=-1) /
+          v64[:, :, 0].abs().amax(dim=-1).clamp_min(1e-30))
+    assert float(e0.max()) <= tol, f"row 0 of o vs V[0]: worst head {float(e0.max()):.3e}"
+    dk64, dv64 = grads[1].double(), grads[2].double()
+    sdv, so = dv64.sum(dim=2), o64.sum(dim=2)
+    edv = (sdv - so).abs().amax(dim=-1) / so.abs().amax(dim=-1)
+    assert float(edv.max()) <= tol, f"sum dV vs sum dO: worst head {float(edv.max()):.3e}"
+    N = o.shape[2]
+    edk = dk64.sum(dim=2).abs().amax(dim=-1) / (N * dk64.abs().amax(dim=(-1, -2)))
+    assert float(edk.max()) <= tol, f"sum dK: worst head {float(edk.max()):.3e}"
+    assert e0.shape == (B, H)
+
+
+def _grid_heads(B, H):
+    """Flat heads covering every XCD (workgroup b runs on XCD b % 8 and takes
+    heads b % 8, b % 8 + 8, ...) and every position in the forward's groups of
+    8 and the backward's groups of 4 heads per XCD: head x + 8 x (first group,
+    position x) and head x + 8 (n - 1 - x) (last group), as (b, h)."""
+    n = (B * H) // 8
+    flat = sorted({x + 8 * min(x, n - 1) for x in range(8)} |
+                  {x + 8 * max(n - 1 - x, 0) for x in range(8)})
+    return [(f // H, f % H) for f in flat if f < B * H]
 
 
 SMALL = [(1, 1, 1), (1, 1, 2), (1, 1, 17), (2, 3, 63), (1, 2, 64), (1, 2, 65), (1, 1, 127),
@@ -243,32 +287,39 @@ def test_fp32_2k_fwd():
     q, k, v = (to_dev(getattr(a, x), "f32") for x in "qkv")
     o, lse = run_fwd(q, k, v, S, guard=False)
     torch.cuda.synchronize()
-    _check_fwd(a, o, lse, sel=[(0, 0), (1, 9), (3, 15)])
+    _check_fwd(a, o, lse, sel=_grid_heads(4, 16))
 
 
 def test_bf16_4k_fwd_bwd():
-    """bfloat16 fwd + bwd at full size (8 x 32 heads x 4096 tokens); sampled heads."""
+    """bfloat16 fwd + bwd at full size (8 x 32 heads x 4096 tokens), in the
+    launch configuration the bench times: 16 heads covering every XCD and every
+    position of the forward's and backward's head groups checked in full
+    against the oracle, and every head against the per-head invariants."""
     a = inp.workload("bf16_4k")
     note("bf16_4k fwd+bwd full size")
     q, k, v = (to_dev(getattr(a, x), "bf16") for x in "qkv")
     o, lse = run_fwd(q, k, v, S, guard=False)
     grads = run_bwd(q, k, v, o, o, lse, S, guard=False)
     torch.cuda.synchronize()
-    sel = [(0, 0), (7, 31)]
+    _check_all_heads(a, o, lse, grads, TOL["bf16"])
+    sel = _grid_heads(8, 32)
+    assert len(sel) == 16
     _check_fwd(a, o, lse, sel=sel)
     _check_bwd(a, grads, sel=sel)
 
 
 def test_bf16_32k_fwd_bwd():
     """bfloat16 fwd + bwd at full size (16 heads x 32768 tokens, q and k scaled
-    by 2: peaked rows); one sampled head checked in full."""
+    by 2: peaked rows); three heads (XCDs 0, 3 and 7) checked in full, every
+    head against the per-head invariants."""
     a = inp.workload("bf16_32k")
     note("bf16_32k fwd+bwd full size")
     q, k, v = (to_dev(getattr(a, x), "bf16") for x in "qkv")
     o, lse = run_fwd(q, k, v, S, guard=False)
     grads = run_bwd(q, k, v, o, o, lse, S, guard=False)
     torch.cuda.synchronize()
-    sel = [(0, 11)]
+    _check_all_heads(a, o, lse, grads, TOL["bf16"])
+    sel = [(0, 0), (0, 11), (0, 15)]
     _check_fwd(a, o, lse, sel=sel)
     _check_bwd(a, grads, sel=sel)
 
