@@ -47,6 +47,9 @@ def lib() -> ctypes.CDLL:
         L.attn_causal_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
                                       vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_causal_bwd.restype = ctypes.c_int
+        L.attn_causal_bwd_noalloc.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
+                                              vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.attn_causal_bwd_noalloc.restype = ctypes.c_int
         L.attn_fwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
                                i64, vp, vp, vp, vp, vp, vp]
         L.attn_fwd.restype = ctypes.c_int
@@ -194,10 +197,11 @@ def attn_causal_bwd_workspace_bytes(dtype_code: int, B: int, H: int, N: int, D: 
     return int(lib().attn_causal_bwd_workspace_bytes(dtype_code, B, H, N, D))
 
 
-def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, need=None):
+def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, need=None, own_workspace=True):
     """Validate the backward's tensors (lse and the gradients included) and
     allocate the outputs and workspace not given.  ``need`` is the workspace
-    size in bytes (the library's own figure when None)."""
+    size in bytes (the library's own figure when None); with
+    ``own_workspace=False`` there is none (returned as None)."""
     import torch
     B, H, N, D = _bhnd(q, "q")
     code = _dtype_code(q)
@@ -209,6 +213,8 @@ def _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, need=None):
     dv = torch.empty_like(q) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _same(t, q, name, "q")
+    if not own_workspace:
+        return (code, B, H, N, D), dq, dk, dv, None
     if workspace is None:
         if need is None:
             need = attn_causal_bwd_workspace_bytes(code, B, H, N, D)
@@ -225,6 +231,23 @@ def attn_causal_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, dq=None
     _check(lib().attn_causal_bwd(code, B, H, N, D, float(scale), _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(q, stream)))
+    return dq, dk, dv
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # ATTN_NOALLOC_SCRATCH_BYTES of include/attn.h
+
+
+def attn_causal_bwd_noalloc(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, dq=None,
+                            dk=None, dv=None, stream=None):
+    """attn_causal_bwd with the library's static per-GPU scratch as workspace
+    (the C call allocates nothing; outputs not given are allocated here by
+    torch).  Calls that can overlap on one GPU race on that scratch."""
+    _on_gpu(q, "q")
+    (code, B, H, N, D), dq, dk, dv, _ = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, None,
+                                                  own_workspace=False)
+    _check(lib().attn_causal_bwd_noalloc(code, B, H, N, D, float(scale), _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), _stream(q, stream)))
     return dq, dk, dv
 
 
@@ -416,7 +439,8 @@ def attn_set_kernel_timer(slot: int, start, stop):
     _check(lib().attn_set_kernel_timer(slot, h(start), h(stop)))
 
 
-__all__ = ["attn_causal_fwd", "attn_causal_bwd", "attn_causal_bwd_workspace_bytes", "attn_fwd",
+__all__ = ["attn_causal_fwd", "attn_causal_bwd", "attn_causal_bwd_workspace_bytes",
+           "attn_causal_bwd_noalloc", "attn_fwd",
            "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_train", "attn_bwd_from_fwd", "MASKS",
            "nw_gauss_average", "attn_matrix_to_table", "attn_table_to_matrix",
            "attn_table_workspace_bytes", "attn_qkv_project", "attn_set_kernel_timer",

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/attn.h"
@@ -201,9 +202,61 @@ int bwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
   return hip_status(e, "backward launch");
 }
 
+// ---- the allocation-free backward ------------------------------------------
+//
+// attn_causal_bwd_noalloc runs the backward with its workspace in this
+// statically allocated device array instead of a caller buffer.  Each GPU the
+// library runs on holds its own copy for the life of the process.  The host
+// name `scratch` is only a stand-in for the device symbol: host code uses the
+// address hipGetSymbolAddress returns for the current device, never the name.
+constexpr size_t kScratchBytes = ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_at[kMaxDevices] = {};  // scratch's device address, per device
+
+// scratch's address on the current device, looked up once per device.
+int scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipError_t e = hipGetDevice(&dev)) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(ATTN_EUNSUPPORTED, "device %d: the scratch table holds %d devices", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_at[dev]) {
+    void* p = nullptr;
+    if (hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)))
+      return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(ATTN_EHIP, "hipGetSymbolAddress(scratch) returned a null address");
+    g_scratch_at[dev] = p;
+  }
+  *out = g_scratch_at[dev];
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int attn_causal_bwd_noalloc(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D,
+                            double scale, const void* q, const void* k, const void* v,
+                            const void* o, const void* dout, const void* lse, void* dq, void* dk,
+                            void* dv, void* stream) {
+  if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
+  const size_t need = workspace_bytes_for(dtype, B * H, N);
+  if (need > kScratchBytes)
+    return fail(ATTN_EINVAL,
+                "B*H*N = %lld rows need %zu bytes of backward workspace; the static scratch "
+                "holds %zu (use attn_causal_bwd with a caller workspace)",
+                (long long)(B * H * N), need, kScratchBytes);
+  void* ws = nullptr;
+  if (int rc = scratch_on_current_device(&ws)) return rc;
+  // every per-row value the kernels read is written first by the backward's
+  // own per-row pass, so the scratch needs no clearing between calls
+  return bwd_impl(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, q, k, v, o, dout, lse, dq, dk,
+                  dv, ws, kScratchBytes, false, (hipStream_t)stream);
+}
 
 int attn_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, attn_mask_t mask,
              int64_t window, const void* q, const void* k, const void* v, void* o, void* lse,

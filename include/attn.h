@@ -117,6 +117,29 @@ ATTN_API int attn_causal_bwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N
                     const void* dout, const void* lse, void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* The backward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * attn_causal_bwd with the same arguments minus the workspace.  Its
+ * workspace is a static device array of ATTN_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; the call
+ * itself allocates nothing.
+ *   - Sizes whose workspace (attn_causal_bwd_workspace_bytes) exceeds
+ *     ATTN_NOALLOC_SCRATCH_BYTES are refused with ATTN_EINVAL before any
+ *     launch: up to 2,096,896 rows (B*H*N) for bfloat16 and float64
+ *     (8 bytes of workspace per row), 4,193,792 for float32 (4 bytes).
+ *   - All calls on one GPU share that GPU's array: two calls whose work can
+ *     overlap on one GPU (different streams, or different host threads) race
+ *     and give wrong gradients.  Calls on one stream are ordered and safe.
+ *   - The array of the device current at the call is used; the stream must
+ *     belong to that device.  Nothing in the array needs clearing between
+ *     calls (the backward writes every value before reading it).
+ * Returns ATTN_OK / ATTN_EINVAL / ATTN_EUNSUPPORTED / ATTN_EHIP. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+ATTN_API int attn_causal_bwd_noalloc(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D,
+                                     double scale, const void* q, const void* k, const void* v,
+                                     const void* o, const void* dout, const void* lse, void* dq,
+                                     void* dk, void* dv, void* stream);
+
 /* Workspace bytes for attn_bwd (the same for every mask; equal to
  * attn_causal_bwd_workspace_bytes). */
 ATTN_API size_t attn_bwd_workspace_bytes(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D);

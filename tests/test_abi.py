@@ -29,7 +29,8 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     assert declared_symbols() == sorted(["attn_causal_fwd", "attn_causal_bwd",
-                                         "attn_causal_bwd_workspace_bytes", "attn_fwd",
+                                         "attn_causal_bwd_workspace_bytes",
+                                         "attn_causal_bwd_noalloc", "attn_fwd",
                                          "attn_bwd", "attn_bwd_workspace_bytes",
                                          "attn_fwd_train", "attn_bwd_from_fwd",
                                          "nw_gauss_average", "attn_set_kernel_timer",
@@ -395,3 +396,19 @@ def test_binding_rejects_bad_loss(loss):
     q, k, v = _qkv()
     with pytest.raises(ValueError, match="loss"):
         csa._train_args(q, k, v, None, None, torch.empty(64, dtype=torch.uint8), loss)
+
+
+def test_noalloc_refuses_sizes_past_its_scratch(L):
+    """attn_causal_bwd_noalloc checks sizes, then whether the workspace fits
+    the static scratch (ATTN_NOALLOC_SCRATCH_BYTES = 16 MiB), before it looks
+    at the device or the pointers."""
+    text = open(HEADER).read()
+    assert "#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert csa.NOALLOC_SCRATCH_BYTES == 16 << 20
+    for dtype, rows in ((csa.ATTN_BF16, 2096896), (csa.ATTN_F64, 2096896), (csa.ATTN_F32, 4193792)):
+        assert L.attn_causal_bwd_workspace_bytes(dtype, 1, 1, rows, 64) <= csa.NOALLOC_SCRATCH_BYTES
+        assert L.attn_causal_bwd_workspace_bytes(dtype, 1, 1, rows + 32, 64) > csa.NOALLOC_SCRATCH_BYTES
+        rc = L.attn_causal_bwd_noalloc(dtype, 1, 1, rows + 32, 64, 0.125, *([None] * 9), None)
+        assert rc == csa.ATTN_EINVAL and "static scratch" in csa.attn_last_error()
+    assert L.attn_causal_bwd_noalloc(csa.ATTN_BF16, 1, 1, 16, 32, 0.125, *([None] * 9), None) \
+        == csa.ATTN_EUNSUPPORTED
