@@ -31,6 +31,11 @@ causal one):
 * ``"window"``: q.t >= k.t AND q.t - k.t < window, a causal band of ``window``
   keys per query (window >= 1).
 
+``seg`` (one integer per token, or None) adds an equality to any of these
+join conditions: the pair (i, j) exists only when seg[i] == seg[j], as when
+the join also matches a segment column (packed documents that must not see
+one another are the usual case).  Ids need not be sorted or contiguous.
+
 The scale is an argument; the pages fix it at 1/8 (= 1/sqrt(64)).  Dividing by
 8 and multiplying by 0.125 give the same float64 result, since 0.125 is a power
 of two.
@@ -77,16 +82,31 @@ def _check_mask(mask: str, window: int) -> None:
         raise ValueError("window must be >= 1")
 
 
-def _present(r0: int, r1: int, ncols: int, mask: str = "causal", window: int = 0) -> np.ndarray:
+def _present(r0: int, r1: int, ncols: int, mask: str = "causal", window: int = 0,
+             seg=None) -> np.ndarray:
     """Boolean (r1-r0, ncols) table of the pairs that exist for queries
-    r0 .. r1-1 and keys 0 .. ncols-1 under the mask's join predicate."""
+    r0 .. r1-1 and keys 0 .. ncols-1 under the mask's join predicate, and,
+    with segment ids, only between tokens of one segment."""
     i = np.arange(r0, r1)[:, None]
     j = np.arange(ncols)[None, :]
     if mask == "causal":
-        return j <= i
-    if mask == "full":
-        return np.ones((r1 - r0, ncols), dtype=bool)
-    return (j <= i) & (i - j < window)
+        p = j <= i
+    elif mask == "full":
+        p = np.ones((r1 - r0, ncols), dtype=bool)
+    else:
+        p = (j <= i) & (i - j < window)
+    if seg is not None:
+        p = p & (seg[r0:r1, None] == seg[None, :ncols])
+    return p
+
+
+def _check_seg(seg, n: int):
+    if seg is None:
+        return None
+    seg = np.asarray(seg)
+    if seg.shape != (n,) or not np.issubdtype(seg.dtype, np.integer):
+        raise ValueError("seg must hold one integer per token")
+    return seg
 
 
 def _key_cols(r1: int, n: int, mask: str) -> int:
@@ -113,13 +133,14 @@ def _sum_present(weights: np.ndarray, present: np.ndarray, values: np.ndarray) -
 
 def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                  scale: float = DEFAULT_SCALE, block: int = 256, mask: str = "causal",
-                 window: int = 0):
-    """Window spelling, matrix form.  q, k, v: (N, D) float64.
+                 window: int = 0, seg=None):
+    """Window spelling, matrix form.  q, k, v: (N, D) float64; seg: (N,) ints or None.
 
     Returns (o, lse, m, z): o (N, D), and per-row lse, max m, denominator z."""
     _check_mask(mask, window)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     n = q.shape[0]
+    seg = _check_seg(seg, n)
     o = np.empty_like(q)
     lse = np.empty(n)
     m_all = np.empty(n)
@@ -127,7 +148,7 @@ def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     for r0 in range(0, n, block):
         r1 = min(n, r0 + block)
         nc = _key_cols(r1, n, mask)
-        present = _present(r0, r1, nc, mask, window)
+        present = _present(r0, r1, nc, mask, window, seg)
         s = (q[r0:r1] @ k[:nc].T) * scale                       # s_ij for every (i, j) of the block
         m = np.max(np.where(present, s, -np.inf), axis=1)       # m_i over present pairs only
         with np.errstate(invalid="ignore", over="ignore"):
@@ -142,7 +163,7 @@ def forward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 def forward_head_relational(q: np.ndarray, k: np.ndarray, v: np.ndarray,
                             scale: float = DEFAULT_SCALE, spelling: str = "group by",
-                            mask: str = "causal", window: int = 0):
+                            mask: str = "causal", window: int = 0, seg=None):
     """The same attention computed over an explicit list of the pairs that
     exist, the way the demo script's two views (``ATTENTION_WINDOW`` and
     ``ATTENTION_GROUP_BY``) treat their join: one record per pair (i, j), and
@@ -157,7 +178,7 @@ def forward_head_relational(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     _check_mask(mask, window)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     n, d = q.shape
-    rows, cols = np.nonzero(_present(0, n, n, mask, window))  # the pair records (i, j)
+    rows, cols = np.nonzero(_present(0, n, n, mask, window, _check_seg(seg, n)))  # pair records
     s = np.einsum("pd,pd->p", q[rows], k[cols]) * scale      # one score per record
     if spelling == "group by":
         best = np.full(n, -np.inf)
@@ -192,15 +213,16 @@ def loss(o: np.ndarray) -> float:
 
 def backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray | None = None,
                   scale: float = DEFAULT_SCALE, block: int = 256, route_max: bool = False,
-                  mask: str = "causal", window: int = 0):
+                  mask: str = "causal", window: int = 0, seg=None):
     """Gradients (dq, dk, dv) of sum_{i,d} dout_id * o_id; with dout = o (the
     default) that is the gradient of loss = sum(o^2) / 2.  Closed-form chain
     rule over the naive plan, recomputing each block's full score rows."""
     _check_mask(mask, window)
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     n = q.shape[0]
+    seg = _check_seg(seg, n)
     if dout is None:
-        dout = forward_head(q, k, v, scale, block, mask, window)[0]
+        dout = forward_head(q, k, v, scale, block, mask, window, seg)[0]
     dout = np.asarray(dout, dtype=np.float64)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -208,7 +230,7 @@ def backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray 
     for r0 in range(0, n, block):
         r1 = min(n, r0 + block)
         nc = _key_cols(r1, n, mask)
-        present = _present(r0, r1, nc, mask, window)
+        present = _present(r0, r1, nc, mask, window, seg)
         s = (q[r0:r1] @ k[:nc].T) * scale
         masked = np.where(present, s, -np.inf)
         m = masked.max(axis=1)
@@ -230,21 +252,28 @@ def backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray 
 
 
 def _map_heads(fn, arrays, workers):
+    """fn(per-head arrays..., batch index) over every (b, h) head."""
     b, h = arrays[0].shape[:2]
     jobs = [(bi, hi) for bi in range(b) for hi in range(h)]
     if workers is None or workers <= 1:
-        return jobs, [fn(*(a[bi, hi] for a in arrays)) for bi, hi in jobs]
+        return jobs, [fn(*(a[bi, hi] for a in arrays), bi) for bi, hi in jobs]
     with ThreadPoolExecutor(max_workers=workers) as ex:
-        return jobs, list(ex.map(lambda j: fn(*(a[j[0], j[1]] for a in arrays)), jobs))
+        return jobs, list(ex.map(lambda j: fn(*(a[j[0], j[1]] for a in arrays), j[0]), jobs))
+
+
+def _seg_of(seg, b):
+    return None if seg is None else np.asarray(seg)[b]
 
 
 def forward(q, k, v, scale: float = DEFAULT_SCALE, workers: int | None = None, block: int = 256,
-            mask: str = "causal", window: int = 0):
-    """[B, H, N, D] float64 -> (o [B, H, N, D], lse [B, H, N]); heads are independent."""
+            mask: str = "causal", window: int = 0, seg=None):
+    """[B, H, N, D] float64 -> (o [B, H, N, D], lse [B, H, N]); heads are
+    independent; seg, if given, is [B, N] (every head of a batch shares it)."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     o = np.empty_like(q)
     lse = np.empty(q.shape[:3])
-    jobs, res = _map_heads(lambda a, b_, c: forward_head(a, b_, c, scale, block, mask, window),
+    jobs, res = _map_heads(lambda a, b_, c, bi: forward_head(a, b_, c, scale, block, mask, window,
+                                                              _seg_of(seg, bi)),
                            (q, k, v), workers)
     for (bi, hi), (oh, lh, _, _) in zip(jobs, res):
         o[bi, hi] = oh
@@ -253,16 +282,17 @@ def forward(q, k, v, scale: float = DEFAULT_SCALE, workers: int | None = None, b
 
 
 def backward(q, k, v, dout=None, scale: float = DEFAULT_SCALE, workers: int | None = None,
-             block: int = 256, mask: str = "causal", window: int = 0):
+             block: int = 256, mask: str = "causal", window: int = 0, seg=None):
     """[B, H, N, D] float64 -> (dq, dk, dv); dout defaults to the oracle's own o."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     if dout is None:
         arrays = (q, k, v)
-        fn = lambda a, b_, c: backward_head(a, b_, c, None, scale, block, mask=mask, window=window)
+        fn = lambda a, b_, c, bi: backward_head(a, b_, c, None, scale, block, mask=mask,
+                                                window=window, seg=_seg_of(seg, bi))
     else:
         arrays = (q, k, v, np.asarray(dout, dtype=np.float64))
-        fn = lambda a, b_, c, d_: backward_head(a, b_, c, d_, scale, block, mask=mask,
-                                                window=window)
+        fn = lambda a, b_, c, d_, bi: backward_head(a, b_, c, d_, scale, block, mask=mask,
+                                                    window=window, seg=_seg_of(seg, bi))
     out = [np.empty_like(q) for _ in range(3)]
     jobs, res = _map_heads(fn, arrays, workers)
     for (bi, hi), grads in zip(jobs, res):

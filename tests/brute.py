@@ -23,16 +23,21 @@ def causal(i, n):
     return list(range(i + 1))
 
 
-def pairs(mask="causal", window=0):
+def pairs(mask="causal", window=0, seg=None):
     """The list of keys query i may see, per join predicate: causal (j <= i),
-    full (every key), window (j <= i and i - j < window)."""
+    full (every key), window (j <= i and i - j < window); with segment ids,
+    only the keys whose id equals the query's."""
     if mask == "causal":
-        return causal
-    if mask == "full":
-        return lambda i, n: list(range(n))
-    if mask == "window":
-        return lambda i, n: list(range(max(0, i - window + 1), i + 1))
-    raise ValueError(mask)
+        base = causal
+    elif mask == "full":
+        base = lambda i, n: list(range(n))
+    elif mask == "window":
+        base = lambda i, n: list(range(max(0, i - window + 1), i + 1))
+    else:
+        raise ValueError(mask)
+    if seg is None:
+        return base
+    return lambda i, n: [j for j in base(i, n) if seg[j] == seg[i]]
 
 
 def attention(q, k, v, scale=0.125, keys=causal):

@@ -461,6 +461,123 @@ def check_batched_heads(orc):
                 assert rel_err(g, scale_d * w) < 1e-14, (workers, scale_d)
 
 
+# --------------------------------------------------------------- segments --
+# An equality on a segment column added to the join: pair (i, j) exists only
+# when seg[i] == seg[j] (and the base predicate admits it).
+
+SEG_MASKS = (("causal", 0), ("full", 0), ("window", 3))
+
+
+def check_seg_brute_force(orc):
+    """50-digit brute force over each predicate's pair list with unsorted,
+    non-contiguous segment ids."""
+    for mask, window, n, d, seed in (("causal", 0, 11, 8, 90), ("full", 0, 10, 5, 91),
+                                     ("window", 3, 12, 6, 92)):
+        rng = _rng(seed)
+        q, k, v = (rng.normal(size=(n, d)) for _ in range(3))
+        seg = rng.integers(0, 3, size=n)
+        o, lse = orc.forward_head(q, k, v, S, block=4, mask=mask, window=window, seg=seg)[:2]
+        bo, bl = brute.attention(q, k, v, S, keys=brute.pairs(mask, window, seg))
+        assert rel_err(o, brute.to_np(bo)) < 2e-14, ("o", mask, n)
+        assert rel_err(lse, brute.to_np(bl)) < 2e-14, ("lse", mask, n)
+
+
+def check_seg_decomposition(orc):
+    """Contiguous segments are independent attentions: each segment's rows of o,
+    lse and of every gradient equal the same attention run on that segment
+    alone.  Interleaved ids (0, 1, 0, 1, ...) are two attentions over the
+    gathered even and odd tokens, in order."""
+    rng = _rng(93)
+    n = 53
+    q, k, v = (rng.normal(size=(n, 64)) * 1.5 for _ in range(3))
+    bounds = [0, 17, 18, 40, n]
+    seg = np.repeat(np.arange(4) * 7 - 3, np.diff(bounds))
+    inter = np.arange(n) % 2
+    for mask, window in SEG_MASKS:
+        o, lse = orc.forward_head(q, k, v, S, block=9, mask=mask, window=window, seg=seg)[:2]
+        grads = orc.backward_head(q, k, v, None, S, block=9, mask=mask, window=window, seg=seg)
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            oa, la = orc.forward_head(q[a:b], k[a:b], v[a:b], S, mask=mask, window=window)[:2]
+            assert rel_err(o[a:b], oa) < 1e-14 and rel_err(lse[a:b], la) < 1e-14, (mask, a)
+            ga = orc.backward_head(q[a:b], k[a:b], v[a:b], None, S, mask=mask, window=window)
+            for g, w in zip(grads, ga):
+                assert rel_err(g[a:b], w) < 1e-13, (mask, a)
+        if mask == "window":
+            continue  # the band counts positions, which gathering renumbers
+        o, lse = orc.forward_head(q, k, v, S, block=9, mask=mask, window=window, seg=inter)[:2]
+        for par in (0, 1):
+            idx = np.nonzero(inter == par)[0]
+            oa, la = orc.forward_head(q[idx], k[idx], v[idx], S, mask=mask)[:2]
+            assert rel_err(o[idx], oa) < 1e-14 and rel_err(lse[idx], la) < 1e-14, (mask, par)
+
+
+def check_seg_inf_and_means(orc):
+    """An infinity in V at key j reaches exactly the rows whose pair with j
+    exists; with Q = 0 each row is the mean of the V rows it may see and lse is
+    the log of their count; one segment for every token is no segment."""
+    rng = _rng(94)
+    n = 40
+    q, k, v = (rng.normal(size=(n, 64)) for _ in range(3))
+    seg = rng.integers(0, 4, size=n)
+    for mask, window in SEG_MASKS:
+        keys = brute.pairs(mask, window, seg)
+        sees = np.zeros((n, n), dtype=bool)
+        for i in range(n):
+            sees[i, keys(i, n)] = True
+        j, col = 13, 7
+        vi = v.copy()
+        vi[j, col] = np.inf
+        o = orc.forward_head(q, k, vi, S, block=8, mask=mask, window=window, seg=seg)[0]
+        assert np.array_equal(np.isposinf(o[:, col]), sees[:, j]), mask
+        assert np.isfinite(np.delete(o, col, axis=1)).all() and np.isfinite(o[~sees[:, j]]).all()
+        o, lse = orc.forward_head(np.zeros((n, 64)), k, v, S, block=8, mask=mask, window=window,
+                                  seg=seg)[:2]
+        want = np.array([v[sees[i]].mean(axis=0) for i in range(n)])
+        assert rel_err(o, want) < 1e-14 and rel_err(lse, np.log(sees.sum(axis=1))) < 1e-15
+        one = orc.forward_head(q, k, v, S, mask=mask, window=window, seg=np.full(n, 5))[0]
+        assert rel_err(one, orc.forward_head(q, k, v, S, mask=mask, window=window)[0]) == 0.0
+
+
+def check_seg_grad_brute_fd(orc):
+    """Gradients under segment predicates against 50-digit central differences
+    of the brute-force forward."""
+    for mask, window, n, d, seed in (("causal", 0, 6, 3, 95), ("full", 0, 5, 3, 96)):
+        rng = _rng(seed)
+        q, k, v = (rng.normal(size=(n, d)) * 1.5 for _ in range(3))
+        seg = np.array([2, 0, 2, 2, 0, 1][:n])
+        got = orc.backward_head(q, k, v, None, S, block=2, mask=mask, window=window, seg=seg)
+        want = brute.grad_fd(q, k, v, S, keys=brute.pairs(mask, window, seg))
+        for name, g, w in zip("qkv", got, want):
+            assert rel_err(g, w) < 1e-13, ("d" + name, mask, rel_err(g, w))
+
+
+def check_seg_spellings_and_batches(orc):
+    """The relational spellings agree with the matrix form under segments, and
+    the batched wrappers apply batch b's ids to every head of batch b."""
+    rng = _rng(97)
+    n = 30
+    q, k, v = (rng.normal(size=(n, 64)) for _ in range(3))
+    seg = rng.integers(0, 3, size=n)
+    for mask, window in SEG_MASKS:
+        o, lse = orc.forward_head(q, k, v, S, block=7, mask=mask, window=window, seg=seg)[:2]
+        for spelling in ("window", "group by"):
+            o2, l2 = orc.forward_head_relational(q, k, v, S, spelling, mask=mask, window=window,
+                                                 seg=seg)
+            assert rel_err(o2, o) < 1e-14 and rel_err(l2, lse) < 1e-14, (mask, spelling)
+    qb, kb, vb = (rng.normal(size=(2, 2, 12, 8)) for _ in range(3))
+    segb = np.array([[0, 0, 1, 1, 1, 0, 2, 2, 0, 1, 1, 2], [1, 1, 1, 0, 0, 0, 0, 1, 1, 1, 0, 0]])
+    o, lse = orc.forward(qb, kb, vb, S, workers=2, seg=segb)
+    grads = orc.backward(qb, kb, vb, None, S, workers=2, seg=segb)
+    for bi in range(2):
+        for hi in range(2):
+            keys = brute.pairs("causal", 0, segb[bi])
+            bo, bl = brute.attention(qb[bi, hi], kb[bi, hi], vb[bi, hi], S, keys=keys)
+            assert rel_err(o[bi, hi], brute.to_np(bo)) < 1e-14, (bi, hi)
+            want = orc.backward_head(qb[bi, hi], kb[bi, hi], vb[bi, hi], None, S, seg=segb[bi])
+            for g, w in zip(grads, want):
+                assert rel_err(g[bi, hi], w) == 0.0, (bi, hi)
+
+
 ATTENTION_FORWARD_CHECKS = [check_brute_force, check_worked_example, check_token0,
                             check_equal_scores, check_rows_sum_to_one, check_prefix,
                             check_linearity, check_k_shift, check_inf_rule, check_spellings_agree]
@@ -472,5 +589,7 @@ MASK_CHECKS = [check_mask_brute_force, check_window_limits, check_mask_equal_sco
                check_mask_grad_invariants]
 LOSS_CHECKS = [check_loss_values, check_loss_brute, check_loss_gradient]
 BATCH_CHECKS = [check_batched_heads]
+SEG_CHECKS = [check_seg_brute_force, check_seg_decomposition, check_seg_inf_and_means,
+              check_seg_grad_brute_fd, check_seg_spellings_and_batches]
 ALL_CHECKS = (ATTENTION_FORWARD_CHECKS + ATTENTION_BACKWARD_CHECKS + NW_CHECKS + MASK_CHECKS
-              + LOSS_CHECKS + BATCH_CHECKS)
+              + LOSS_CHECKS + BATCH_CHECKS + SEG_CHECKS)

@@ -28,8 +28,8 @@ def _load(fname, edit):
 
 # (file, (old text, new text, which occurrence), checks that should catch it)
 MUTANTS = {
-    "diagonal dropped": ("attention.py", ("return j <= i", "return j < i", 0), "fwd"),
-    "one token of lookahead": ("attention.py", ("return j <= i", "return j <= i + 1", 0), "fwd"),
+    "diagonal dropped": ("attention.py", ("p = j <= i", "p = j < i", 0), "fwd"),
+    "one token of lookahead": ("attention.py", ("p = j <= i", "p = j <= i + 1", 0), "fwd"),
     "scores transposed": ("attention.py", ("(q[r0:r1] @ k[:nc].T)", "(k[r0:r1] @ q[:nc].T)", 0), "fwd"),
     "scale 1/4": ("attention.py", ("@ k[:nc].T) * scale", "@ k[:nc].T) * 0.25", 0), "fwd"),
     "lse in log2": ("attention.py", ("lse[r0:r1] = m + np.log(z)", "lse[r0:r1] = m + np.log2(z)", 0), "fwd"),
@@ -46,14 +46,14 @@ MUTANTS = {
     "dV from v": ("attention.py", ("dv[:nc] += p.T @ dout[r0:r1]", "dv[:nc] += p.T @ v[r0:r1]", 0), "bwd"),
     "dP from k": ("attention.py", ("dout[r0:r1] @ v[:nc].T", "dout[r0:r1] @ k[:nc].T", 0), "bwd"),
     "dS transposed in dQ": ("attention.py", ("(ds @ k[:nc])", "(ds.T[:r1 - r0, :] @ k[:nc])", 0), "bwd"),
-    "backward unmasked": ("attention.py", ("present = _present(r0, r1, nc, mask, window)",
+    "backward unmasked": ("attention.py", ("present = _present(r0, r1, nc, mask, window, seg)",
                                            "present = np.ones((r1 - r0, nc), dtype=bool)", 1), "bwd"),
     "window one key wider": ("attention.py", ("(i - j < window)", "(i - j <= window)", 0), "mask"),
-    "window not causal": ("attention.py", ("return (j <= i) & (i - j < window)",
-                                           "return np.abs(i - j) < window", 0), "mask"),
+    "window not causal": ("attention.py", ("p = (j <= i) & (i - j < window)",
+                                           "p = np.abs(i - j) < window", 0), "mask"),
     "full keeps the causal predicate": ("attention.py",
-                                        ("return np.ones((r1 - r0, ncols), dtype=bool)",
-                                         "return np.broadcast_to(j <= i, (r1 - r0, ncols))", 0),
+                                        ("p = np.ones((r1 - r0, ncols), dtype=bool)",
+                                         "p = np.broadcast_to(j <= i, (r1 - r0, ncols))", 0),
                                         "mask"),
     "full sees only earlier blocks' keys": ("attention.py",
                                             ('return n if mask == "full" else r1', "return r1", 0),
@@ -71,13 +71,26 @@ MUTANTS = {
     "backward ignores dout": ("attention.py", ("arrays = (q, k, v, np.asarray(dout, dtype=np.float64))",
                                                "arrays = (q, k, v, np.asarray(dout, dtype=np.float64) * 0 + q)", 0),
                               "batch_dout"),
+    "segments ignored": ("attention.py", ("p = p & (seg[r0:r1, None] == seg[None, :ncols])",
+                                          "p = p", 0), "seg"),
+    "segments ordered instead of equal": ("attention.py",
+                                          ("(seg[r0:r1, None] == seg[None, :ncols])",
+                                           "(seg[r0:r1, None] >= seg[None, :ncols])", 0), "seg"),
+    "key segments shifted by one": ("attention.py", ("seg[None, :ncols])",
+                                                     "np.roll(seg, 1)[None, :ncols])", 0), "seg"),
+    "batch 0's segments for every batch": ("attention.py", ("np.asarray(seg)[b]",
+                                                            "np.asarray(seg)[0]", 0), "seg"),
+    "backward ignores segments": ("attention.py", ("present = _present(r0, r1, nc, mask, window, seg)",
+                                                   "present = _present(r0, r1, nc, mask, window)", 1),
+                                  "seg"),
     "bandwidth 2h^2": ("nw.py", ("/ denom", "/ (2 * denom)", 0), "nw"),
     "y against x": ("nw.py", ("(ty[r0:r1, None] - sy[None, :])", "(ty[r0:r1, None] - sx[None, :])", 0), "nw"),
     "mean of weights": ("nw.py", ("(w @ sv) / w.sum(axis=1)", "(w @ sv) / w.shape[1]", 0), "nw"),
     "min subtracted": ("nw.py", ("e.max(axis=1, keepdims=True)", "e.min(axis=1, keepdims=True)", 0), "nw"),
 }
 
-GROUPS = {"loss": oracle_pins.LOSS_CHECKS,
+GROUPS = {"seg": oracle_pins.SEG_CHECKS,
+          "loss": oracle_pins.LOSS_CHECKS,
           "batch": oracle_pins.BATCH_CHECKS,
           "batch_dout": oracle_pins.BATCH_CHECKS,
           "fwd": oracle_pins.ATTENTION_FORWARD_CHECKS,
