@@ -98,12 +98,13 @@ def make_inputs(name):
 
 
 def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask="causal",
-                   window=0, fused=False):
+                   window=0, fused=False, seg=None):
     """Run `steps` timed steps; returns (mean ms per step, wall ms per step,
     {slot: mean ms}, outputs, sorted per-step ms).
     The causal predicate goes through attn_causal_fwd / _bwd, others through
-    attn_fwd / attn_bwd; fused: attn_fwd_train (forward + loss + the
-    backward's per-row values) and attn_bwd_from_fwd."""
+    attn_fwd / attn_bwd, segment ids (seg) through attn_fwd_seg / _bwd_seg;
+    fused: attn_fwd_train (forward + loss + the backward's per-row values) and
+    attn_bwd_from_fwd."""
     import torch
 
     import causal_softmax_attention_amd as csa
@@ -120,7 +121,12 @@ def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask=
     loss = torch.empty(1, dtype=torch.float64, device=q.device)
 
     def step():
-        if fused:
+        if seg is not None:
+            csa.attn_fwd_seg(q, k, v, seg, 0.125, mask, window, o=o, lse=lse)
+            if with_bwd:
+                csa.attn_bwd_seg(q, k, v, o, o, lse, seg, 0.125, mask, window, dq=dq, dk=dk,
+                                 dv=dv, workspace=ws)
+        elif fused:
             csa.attn_fwd_train(q, k, v, 0.125, mask, window, o=o, lse=lse, workspace=ws, loss=loss)
             csa.attn_bwd_from_fwd(q, k, v, o, lse, ws, 0.125, mask, window, dq=dq, dk=dk, dv=dv)
         elif mask == "causal":
@@ -336,6 +342,20 @@ def secondary(steps):
         ms, _, per, _, _ = time_attention(q, k, v, max(2, steps // 2), 1, mask=mask, window=window)
         npairs = B_ * H_ * (N_ * N_ if mask == "full" else
                             sum(min(i + 1, window) for i in range(N_)))
+        fl = 14 * D * npairs
+        out[key] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
+                    "pairs": npairs, "kernels_ms": per}
+    # segment ids on the same inputs (causal): packed documents of mean 512
+    # tokens, and two interleaved ids per row (every tile masked); flops count
+    # the pairs that exist
+    for kind, key in (("packed", "bf16_4k_segments_packed512_fwd_bwd"),
+                      ("interleaved", "bf16_4k_segments_interleaved2_fwd_bwd")):
+        seg = inp.segment_ids(45, B_, N_, kind, mean_len=512, n_ids=2)
+        i = np.arange(N_)
+        npairs = H_ * int(sum(((sg[None, :] == sg[:, None]) & (i[None, :] <= i[:, None])).sum()
+                              for sg in seg))
+        sd = torch.from_numpy(seg).to(q.device)
+        ms, _, per, _, _ = time_attention(q, k, v, max(2, steps // 2), 1, seg=sd)
         fl = 14 * D * npairs
         out[key] = {"ms": ms, "TFLOP/s": fl / ms / 1e9, "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
                     "pairs": npairs, "kernels_ms": per}

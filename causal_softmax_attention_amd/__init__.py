@@ -58,6 +58,12 @@ def lib() -> ctypes.CDLL:
         L.attn_bwd.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double, ctypes.c_int,
                                i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.attn_bwd.restype = ctypes.c_int
+        L.attn_fwd_seg.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
+                                   ctypes.c_int, i64] + [vp] * 7
+        L.attn_fwd_seg.restype = ctypes.c_int
+        L.attn_bwd_seg.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
+                                   ctypes.c_int, i64] + [vp] * 11 + [ctypes.c_size_t, vp]
+        L.attn_bwd_seg.restype = ctypes.c_int
         L.attn_fwd_train.argtypes = [ctypes.c_int, i64, i64, i64, i64, ctypes.c_double,
                                      ctypes.c_int, i64, vp, vp, vp, vp, vp, vp, sz, vp, vp]
         L.attn_fwd_train.restype = ctypes.c_int
@@ -267,6 +273,42 @@ def attn_bwd(q, k, v, o, dout, lse, scale: float = DEFAULT_SCALE, mask: str = "c
     return dq, dk, dv
 
 
+def _check_seg(seg, q):
+    """Segment ids: a contiguous int32 [B, N] tensor on q's device."""
+    import torch
+    B, _, N, _ = q.shape
+    if (tuple(seg.shape) != (B, N) or seg.dtype != torch.int32 or seg.device != q.device
+            or not seg.is_contiguous()):
+        raise ValueError("seg must be a contiguous int32 [B, N] tensor on q's device")
+
+
+def attn_fwd_seg(q, k, v, seg, scale: float = DEFAULT_SCALE, mask: str = "causal",
+                 window: int = 0, o=None, lse=None, stream=None):
+    """attn_fwd with the segment predicate: pair (i, j) also needs
+    seg[b, i] == seg[b, j] (seg: int32 [B, N]); returns (o, lse)."""
+    _on_gpu(q, "q")
+    (B, H, N, D), o, lse = _fwd_args(q, k, v, o, lse)
+    _check_seg(seg, q)
+    _check(lib().attn_fwd_seg(_dtype_code(q), B, H, N, D, float(scale), _mask_code(mask),
+                              int(window), _ptr(seg), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                              _ptr(lse), _stream(q, stream)))
+    return o, lse
+
+
+def attn_bwd_seg(q, k, v, o, dout, lse, seg, scale: float = DEFAULT_SCALE, mask: str = "causal",
+                 window: int = 0, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """attn_bwd with the segment predicate (lse from attn_fwd_seg with the same
+    seg, mask and window); returns (dq, dk, dv)."""
+    _on_gpu(q, "q")
+    (code, B, H, N, D), dq, dk, dv, ws = _bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    _check_seg(seg, q)
+    _check(lib().attn_bwd_seg(code, B, H, N, D, float(scale), _mask_code(mask), int(window),
+                              _ptr(seg), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                              _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                              ws.numel() * ws.element_size(), _stream(q, stream)))
+    return dq, dk, dv
+
+
 def _train_args(q, k, v, o, lse, workspace, loss, need=None):
     """Validate attn_fwd_train's tensors; ``loss`` must be a one-element
     float64 tensor on q's device (the library writes one double there)."""
@@ -442,6 +484,7 @@ def attn_set_kernel_timer(slot: int, start, stop):
 __all__ = ["attn_causal_fwd", "attn_causal_bwd", "attn_causal_bwd_workspace_bytes",
            "attn_causal_bwd_noalloc", "attn_fwd",
            "attn_bwd", "attn_bwd_workspace_bytes", "attn_fwd_train", "attn_bwd_from_fwd", "MASKS",
+           "attn_fwd_seg", "attn_bwd_seg",
            "nw_gauss_average", "attn_matrix_to_table", "attn_table_to_matrix",
            "attn_table_workspace_bytes", "attn_qkv_project", "attn_set_kernel_timer",
            "attn_last_error", "lib", "AttnError",

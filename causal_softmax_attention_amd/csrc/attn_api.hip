@@ -102,14 +102,27 @@ size_t workspace_bytes_for(int dtype, int64_t heads, int64_t N) {
   return parts_offset(dtype, heads, N) + attn::kLossParts * sizeof(double);
 }
 
+// Segment ids [B][N] (int32, one row per batch, shared by its H heads): the
+// pointer must be 4-byte aligned and no output may overlap its B*N*4 bytes.
+int add_segments(const int32_t* seg, int64_t H, attn::Mask& mk) {
+  if ((uintptr_t)seg & 3u) return fail(ATTN_EINVAL, "segment ids must be 4-byte aligned");
+  mk.seg = seg;
+  mk.hpb = (int)H;
+  return ATTN_OK;
+}
+
+size_t seg_bytes(int64_t B, int64_t N) { return (size_t)B * N * sizeof(int32_t); }
+
 // attn_fwd, and with bwd_ws non-null the forward of attn_fwd_train (which
-// checks the workspace itself).
+// checks the workspace itself); seg non-null adds the segment predicate.
 int fwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
-             int64_t window, const void* q, const void* k, const void* v, void* o, void* lse,
-             void* bwd_ws, hipStream_t s) {
+             int64_t window, const int32_t* seg, const void* q, const void* k, const void* v,
+             void* o, void* lse, void* bwd_ws, hipStream_t s) {
   if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
   attn::Mask mk;
   if (int rc = make_mask(mask, window, N, mk)) return rc;
+  if (seg)
+    if (int rc = add_segments(seg, H, mk)) return rc;
   if (!q || !k || !v || !o || !lse) return fail(ATTN_EINVAL, "null pointer argument");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return fail(ATTN_EINVAL, "pointers must be 16-byte aligned");
@@ -121,6 +134,8 @@ int fwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
     if (overlap(o, tb, p, tb) || overlap(lse, lb, p, tb))
       return fail(ATTN_EINVAL, "outputs must not alias inputs");
   if (overlap(o, tb, lse, lb)) return fail(ATTN_EINVAL, "o and lse overlap");
+  if (seg && (overlap(o, tb, seg, seg_bytes(B, N)) || overlap(lse, lb, seg, seg_bytes(B, N))))
+    return fail(ATTN_EINVAL, "outputs must not alias the segment ids");
   if (bwd_ws) {
     const size_t wb = workspace_bytes_for(dtype, heads, N);
     const void* all[] = {q, k, v, o};
@@ -148,12 +163,14 @@ int fwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
 // attn_bwd; prepared: the workspace already holds the per-row values the
 // forward of attn_fwd_train wrote (dout is o).
 int bwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, int mask,
-             int64_t window, const void* q, const void* k, const void* v, const void* o,
-             const void* dout, const void* lse, void* dq, void* dk, void* dv, void* workspace,
-             size_t workspace_bytes, bool prepared, hipStream_t s) {
+             int64_t window, const int32_t* seg, const void* q, const void* k, const void* v,
+             const void* o, const void* dout, const void* lse, void* dq, void* dk, void* dv,
+             void* workspace, size_t workspace_bytes, bool prepared, hipStream_t s) {
   if (int rc = check_sizes(dtype, B, H, N, D, scale)) return rc;
   attn::Mask mk;
   if (int rc = make_mask(mask, window, N, mk)) return rc;
+  if (seg)
+    if (int rc = add_segments(seg, H, mk)) return rc;
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
     return fail(ATTN_EINVAL, "null pointer argument");
   const void* all[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
@@ -176,6 +193,14 @@ int bwd_impl(int dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale
   }
   if (overlap(dq, tb, dk, tb) || overlap(dq, tb, dv, tb) || overlap(dk, tb, dv, tb))
     return fail(ATTN_EINVAL, "dq, dk and dv must not overlap");
+  if (seg) {
+    void* written[] = {dq, dk, dv};
+    for (void* w : written)
+      if (overlap(w, tb, seg, seg_bytes(B, N)))
+        return fail(ATTN_EINVAL, "outputs must not alias the segment ids");
+    if (overlap(workspace, need, seg, seg_bytes(B, N)))
+      return fail(ATTN_EINVAL, "workspace aliases the segment ids");
+  }
   for (const void* r : ins)
     if (overlap(workspace, need, r, tb)) return fail(ATTN_EINVAL, "workspace aliases an input");
   if (overlap(workspace, need, lse, lb)) return fail(ATTN_EINVAL, "workspace aliases lse");
@@ -254,14 +279,22 @@ int attn_causal_bwd_noalloc(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N,
   if (int rc = scratch_on_current_device(&ws)) return rc;
   // every per-row value the kernels read is written first by the backward's
   // own per-row pass, so the scratch needs no clearing between calls
-  return bwd_impl(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, q, k, v, o, dout, lse, dq, dk,
-                  dv, ws, kScratchBytes, false, (hipStream_t)stream);
+  return bwd_impl(dtype, B, H, N, D, scale, ATTN_MASK_CAUSAL, 0, nullptr, q, k, v, o, dout, lse,
+                  dq, dk, dv, ws, kScratchBytes, false, (hipStream_t)stream);
 }
 
 int attn_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale, attn_mask_t mask,
              int64_t window, const void* q, const void* k, const void* v, void* o, void* lse,
              void* stream) {
-  return fwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, lse, nullptr,
+  return fwd_impl(dtype, B, H, N, D, scale, mask, window, nullptr, q, k, v, o, lse, nullptr,
+                  (hipStream_t)stream);
+}
+
+int attn_fwd_seg(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                 attn_mask_t mask, int64_t window, const int32_t* seg, const void* q,
+                 const void* k, const void* v, void* o, void* lse, void* stream) {
+  if (!seg) return fail(ATTN_EINVAL, "null segment ids");
+  return fwd_impl(dtype, B, H, N, D, scale, mask, window, seg, q, k, v, o, lse, nullptr,
                   (hipStream_t)stream);
 }
 
@@ -284,7 +317,17 @@ int attn_bwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, dou
              int64_t window, const void* q, const void* k, const void* v, const void* o,
              const void* dout, const void* lse, void* dq, void* dk, void* dv, void* workspace,
              size_t workspace_bytes, void* stream) {
-  return bwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, dout, lse, dq, dk, dv,
+  return bwd_impl(dtype, B, H, N, D, scale, mask, window, nullptr, q, k, v, o, dout, lse, dq, dk,
+                  dv, workspace, workspace_bytes, false, (hipStream_t)stream);
+}
+
+int attn_bwd_seg(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D, double scale,
+                 attn_mask_t mask, int64_t window, const int32_t* seg, const void* q,
+                 const void* k, const void* v, const void* o, const void* dout, const void* lse,
+                 void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (!seg) return fail(ATTN_EINVAL, "null segment ids");
+  return bwd_impl(dtype, B, H, N, D, scale, mask, window, seg, q, k, v, o, dout, lse, dq, dk, dv,
                   workspace, workspace_bytes, false, (hipStream_t)stream);
 }
 
@@ -317,7 +360,8 @@ int attn_fwd_train(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t 
   if (overlap(loss, 8, lse, lb) || overlap(loss, 8, workspace, need))
     return fail(ATTN_EINVAL, "loss aliases lse or the workspace");
   hipStream_t s = (hipStream_t)stream;
-  if (int rc = fwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, lse, workspace, s))
+  if (int rc = fwd_impl(dtype, B, H, N, D, scale, mask, window, nullptr, q, k, v, o, lse,
+                        workspace, s))
     return rc;
   const int kind = dtype == ATTN_F64 ? 0 : dtype == ATTN_F32 ? 1 : 2;
   double* parts = (double*)((char*)workspace + parts_offset(dtype, heads, N));
@@ -329,7 +373,7 @@ int attn_bwd_from_fwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64
                       attn_mask_t mask, int64_t window, const void* q, const void* k, const void* v,
                       const void* o, const void* lse, void* dq, void* dk, void* dv,
                       void* workspace, size_t workspace_bytes, void* stream) {
-  return bwd_impl(dtype, B, H, N, D, scale, mask, window, q, k, v, o, o, lse, dq, dk, dv,
+  return bwd_impl(dtype, B, H, N, D, scale, mask, window, nullptr, q, k, v, o, o, lse, dq, dk, dv,
                   workspace, workspace_bytes, true, (hipStream_t)stream);
 }
 

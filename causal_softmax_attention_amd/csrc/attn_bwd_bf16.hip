@@ -106,23 +106,30 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
 // frees the previous stage's buffer for stage s+2.  All four waves of a
 // workgroup walk the same halves from the workgroup's first key; halves before
 // a wave's diagonal are fully masked (weight 0), so they add nothing.
-struct alignas(16) QStage {
+// SEG: the stage also holds its queries' segment ids.
+template <bool SEG>
+struct alignas(16) QStageT {
   __bf16 q[kT2 * kD];
   __bf16 dout[kT2 * kD];
   float nlse[kT2];
   float ndelta[kT2];
+  int32_t seg[SEG ? kT2 : 4];
 };
 
+template <bool SEG>
 struct DkdvPipe {
   floatx16 s[kKT], dp[kKT];          // A(n) results, consumed by B(n)
   uint32_t pp[kKT][8], dsp[kKT][8];  // B(n-1) results, consumed by C(n-1)
+  int32_t qs[SEG ? 16 : 1];          // A(n)'s query ids (rows acc_row(r, h)), for B(n)
 };
 
-// A: S' and dP' of the 32 queries at rows row0.. of a stage.
-__device__ __forceinline__ void dkdv_scores(const QStage& st, int row0, int lane,
+// A: S' and dP' of the 32 queries at rows row0.. of a stage (and, with
+// segment ids, the ids of the lane's rows).
+template <bool SEG>
+__device__ __forceinline__ void dkdv_scores(const QStageT<SEG>& st, int row0, int lane,
                                             const bf16x8_t (&kop)[kKT][4],
                                             const bf16x8_t (&vop)[kKT][4], floatx16 (&s)[kKT],
-                                            floatx16 (&dp)[kKT]) {
+                                            floatx16 (&dp)[kKT], int32_t* qs) {
   const int i32 = lane & 31, h = lane >> 5;
   bf16x8_t qa[4], oa[4];
 #pragma unroll
@@ -133,6 +140,10 @@ __device__ __forceinline__ void dkdv_scores(const QStage& st, int row0, int lane
   floatx16 ls, ds;
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
+    if (SEG) {
+      const int4 w = *(const int4*)(st.seg + row0 + 8 * g + 4 * h);
+      qs[4 * g + 0] = w.x; qs[4 * g + 1] = w.y; qs[4 * g + 2] = w.z; qs[4 * g + 3] = w.w;
+    }
     const float4 a = *(const float4*)(st.nlse + row0 + 8 * g + 4 * h);
     const float4 b = *(const float4*)(st.ndelta + row0 + 8 * g + 4 * h);
     ls[4 * g + 0] = a.x; ls[4 * g + 1] = a.y; ls[4 * g + 2] = a.z; ls[4 * g + 3] = a.w;
@@ -155,11 +166,12 @@ __device__ __forceinline__ void dkdv_scores(const QStage& st, int row0, int lane
 // under the causal predicate, query - key >= band under a window) get weight 0
 // (a select).  Queries past the end need no mask: their Q and dO rows read as
 // zeros, so their dS is 0 and their P multiplies a zero dO row.
-template <bool MASKED>
+template <bool MASKED, bool SEG>
 __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[kKT], const floatx16 (&dp)[kKT],
                                              uint32_t (&pp)[kKT][8], uint32_t (&dsp)[kKT][8],
                                              int qrow0, int kw, int lane, float c_scale,
-                                             int causal, int band) {
+                                             int causal, int band, const int32_t* qs,
+                                             int32_t sk) {
   const int i32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int kt = 0; kt < kKT; ++kt) {
@@ -173,7 +185,8 @@ __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[kKT], const flo
         float p = __builtin_amdgcn_exp2f(s[kt][r] * c_scale);
         if (MASKED) {
           const int qi = qrow0 + acc_row(r, h);
-          p = (causal && key > qi) || (band && qi - key >= band) ? 0.f : p;
+          p = (causal && key > qi) || (band && qi - key >= band) || (SEG && qs[r] != sk) ? 0.f
+                                                                                          : p;
         }
         pv[e] = p;
         dsv[e] = p * dp[kt][r];
@@ -185,7 +198,8 @@ __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[kKT], const flo
 }
 
 // C: dV^T += dO^T P and dK^T += Q^T dS over the 32 queries at rows row0.. of a stage.
-__device__ __forceinline__ void dkdv_accum(const QStage& st, int row0, int lane,
+template <class ST>
+__device__ __forceinline__ void dkdv_accum(const ST& st, int row0, int lane,
                                            const uint32_t (&pp)[kKT][8],
                                            const uint32_t (&dsp)[kKT][8],
                                            floatx16 (&dkacc)[2][kKT], floatx16 (&dvacc)[2][kKT]) {
@@ -205,16 +219,18 @@ __device__ __forceinline__ void dkdv_accum(const QStage& st, int row0, int lane,
 
 // One pipelined step: A(n+1) from (sa, ra), B(n) of the half whose first query
 // is qrow0, C(n-1) from (sc, rc).  SKIP_C: there is no half n-1.
-template <bool MASKED, bool SKIP_C>
-__device__ __forceinline__ void dkdv_step(const QStage& sa, int ra, const QStage& sc, int rc,
-                                          int qrow0, int kw, int lane, float c_scale, int causal,
-                                          int band, const bf16x8_t (&kop)[kKT][4],
-                                          const bf16x8_t (&vop)[kKT][4], DkdvPipe& pipe,
-                                          floatx16 (&dkacc)[2][kKT], floatx16 (&dvacc)[2][kKT]) {
+template <bool MASKED, bool SKIP_C, bool SEG>
+__device__ __forceinline__ void dkdv_step(const QStageT<SEG>& sa, int ra, const QStageT<SEG>& sc,
+                                          int rc, int qrow0, int kw, int lane, float c_scale,
+                                          int causal, int band, const bf16x8_t (&kop)[kKT][4],
+                                          const bf16x8_t (&vop)[kKT][4], DkdvPipe<SEG>& pipe,
+                                          floatx16 (&dkacc)[2][kKT], floatx16 (&dvacc)[2][kKT],
+                                          int32_t sk) {
   uint32_t pp[kKT][8], dsp[kKT][8];
   if (!SKIP_C) dkdv_accum(sc, rc, lane, pipe.pp, pipe.dsp, dkacc, dvacc);
-  dkdv_softmax<MASKED>(pipe.s, pipe.dp, pp, dsp, qrow0, kw, lane, c_scale, causal, band);
-  dkdv_scores(sa, ra, lane, kop, vop, pipe.s, pipe.dp);
+  dkdv_softmax<MASKED, SEG>(pipe.s, pipe.dp, pp, dsp, qrow0, kw, lane, c_scale, causal, band,
+                            pipe.qs, sk);
+  dkdv_scores<SEG>(sa, ra, lane, kop, vop, pipe.s, pipe.dp, pipe.qs);
 #pragma unroll
   for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
@@ -228,12 +244,16 @@ __device__ __forceinline__ void dkdv_step(const QStage& sa, int ra, const QStage
 // BANDED: a window of band keys; stages that reach its far edge take the
 // masked body too.
 // Without it the predicate is causal (causal = 1) or absent (causal = 0).
-template <bool BANDED>
+// SEG: only pairs of equal segment ids (seg, [B][N], batch = head / hpb)
+// exist; every stage takes the masked body.
+template <bool BANDED, bool SEG>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ nlseg,
     const float* __restrict__ ndeltag, __bf16* __restrict__ dk, __bf16* __restrict__ dv,
-    int heads, int N, int nkb, float c_scale, float scale, int causal, int band_arg) {
+    int heads, int N, int nkb, float c_scale, float scale, int causal, int band_arg,
+    const int32_t* __restrict__ seg, int hpb) {
+  using QStage = QStageT<SEG>;
   const int band = BANDED ? band_arg : 0;
   __shared__ QStage st0, st1, st2;
   int head, kb;
@@ -278,24 +298,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   const uint32_t tbytes = (uint32_t)N * kD * 2, rbytes = (uint32_t)N * 4;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + base, tbytes), ro = head_rsrc(dout + base, tbytes);
   const __amdgpu_buffer_rsrc_t rl = head_rsrc(nlseg + rbase, rbytes), rd = head_rsrc(ndeltag + rbase, rbytes);
+  const int32_t* segrow = SEG ? seg + (size_t)(head / hpb) * N : nullptr;
+  __amdgpu_buffer_rsrc_t rs = rl;
+  if (SEG) rs = head_rsrc(segrow, rbytes);
+  const int32_t sk = SEG && kw + i32 < N ? segrow[kw + i32] : 0;  // the lane's key id
   auto issue = [&](QStage& s, int t) {
     const int r0 = qstart + t * kT2;
     if (wave == 0) rows_async(rl, s.nlse, r0, lane);
     else if (wave == 1) rows_async(rd, s.ndelta, r0, lane);
+    else if (SEG && wave == 2) rows_async(rs, (float*)s.seg, r0, lane);
     tile_async<kT2, kWaves>(rq, s.q, r0, wave, lane);
     tile_async<kT2, kWaves>(ro, s.dout, r0, wave, lane);
   };
-  DkdvPipe pipe;
+  DkdvPipe<SEG> pipe;
   // stage s: cur holds it, nxt stage s + 1, prv stage s - 1 (and receives s + 2)
   auto stage = [&](auto masked, auto first, QStage& cur, QStage& nxt, QStage& prv, int s) {
     constexpr bool M = decltype(masked)::value, F = decltype(first)::value;
     const int q0 = qstart + s * kT2;
-    dkdv_step<M, F>(cur, 32, prv, 32, q0, kw, lane, c_scale, causal, band, kop, vop, pipe,
-                    dkacc, dvacc);
+    dkdv_step<M, F, SEG>(cur, 32, prv, 32, q0, kw, lane, c_scale, causal, band, kop, vop, pipe,
+                         dkacc, dvacc, sk);
     wait_vm_barrier<0>();  // stage s + 1 has landed; every wave is done with prv
     if (s + 2 < nst) issue(prv, s + 2);
-    dkdv_step<M, false>(nxt, 0, cur, 0, q0 + 32, kw, lane, c_scale, causal, band, kop, vop,
-                        pipe, dkacc, dvacc);
+    dkdv_step<M, false, SEG>(nxt, 0, cur, 0, q0 + 32, kw, lane, c_scale, causal, band, kop, vop,
+                             pipe, dkacc, dvacc, sk);
   };
   // stages 0 and 1 hold the block's diagonal (masked body); later stages lie
   // wholly after every key of the block, so only a window's far edge masks
@@ -307,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   using T = std::true_type;
   using Fl = std::false_type;
   const int edge = BANDED ? (band - kT2 + 1 + kb * kBlk - qstart + kT2 - 1) / kT2 : nst;
-  const int plain_end = BANDED ? 2 + 3 * (max(edge - 2, 0) / 3) : nst;
+  const int plain_end = SEG ? 2 : BANDED ? 2 + 3 * (max(edge - 2, 0) / 3) : nst;
 
   issue(st0, 0);
   if (nst > 1) issue(st1, 1);
@@ -318,7 +343,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
     // 0's last half (issued by stage 1's first step)
     wait_vm_barrier<0>();
     if (2 < nst) issue(st2, 2);
-    dkdv_scores(st1, 0, lane, kop, vop, pipe.s, pipe.dp);
+    dkdv_scores<SEG>(st1, 0, lane, kop, vop, pipe.s, pipe.dp, pipe.qs);
 #pragma unroll
     for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
@@ -327,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
         pipe.dsp[kt][i] = 0u;
       }
   } else {
-    dkdv_scores(st0, 0, lane, kop, vop, pipe.s, pipe.dp);  // A(0)
+    dkdv_scores<SEG>(st0, 0, lane, kop, vop, pipe.s, pipe.dp, pipe.qs);  // A(0)
     stage(T{}, T{}, st0, st1, st2, 0);
   }
   if (nst > 1) stage(T{}, Fl{}, st1, st2, st0, 1);
@@ -337,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
     if (s + 1 < nst) stage(Fl{}, Fl{}, st0, st1, st2, s + 1);
     if (s + 2 < nst) stage(Fl{}, Fl{}, st1, st2, st0, s + 2);
   }
-  if (BANDED) {
+  if (BANDED || SEG) {
     for (; s < nst; s += 3) {
       stage(T{}, Fl{}, st2, st0, st1, s);
       if (s + 1 < nst) stage(T{}, Fl{}, st0, st1, st2, s + 1);
@@ -395,9 +420,11 @@ hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, co
     if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
   }
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
-  auto kern = mk.band > 0 ? bwd_dkdv_bf16<true> : bwd_dkdv_bf16<false>;
+  auto kern = mk.seg ? (mk.band > 0 ? bwd_dkdv_bf16<true, true> : bwd_dkdv_bf16<false, true>)
+                     : (mk.band > 0 ? bwd_dkdv_bf16<true, false> : bwd_dkdv_bf16<false, false>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, dout, nlse, ndelta, dk,
-                     dv, (int)heads, (int)N, nb, c, (float)scale, mk.causal, mk.band);
+                     dv, (int)heads, (int)N, nb, c, (float)scale, mk.causal, mk.band, mk.seg,
+                     mk.hpb);
   if (hipError_t e = mark(tm.stop[kTimerBwdDkdv], stream)) return e;
   if (hipError_t e = hipGetLastError()) return e;
   return launch_bwd_dq_bf16(q, k, v, dout, nlse, ndelta, dq, heads, N, scale, mk, stream, tm);

@@ -31,11 +31,21 @@ constexpr int kT2 = kT;                  // keys per LDS stage
 // query (one per lane), as in the dK/dV pass.  MASKED: the tile holds absent
 // pairs (past the wave's diagonal or a window's start, or past the end of the
 // sequence), which get weight 0 (a select, not a branch).
-template <bool MASKED>
+// SEG: segment ids apply (segk: the tile's 64 key ids in LDS, sq: the lane's
+// query id); a pair of different ids is absent.
+template <bool MASKED, bool SEG>
 __device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[kQT], const floatx16 (&dp)[kQT],
                                                 uint32_t (&dsp)[kQT][8], int kt, int k0, int qw,
                                                 int N, int i32, int h, float c_scale, int causal,
-                                                int band) {
+                                                int band, const int32_t* segk, int32_t sq) {
+  int32_t sk[16];  // ids of the lane's 16 keys of this half
+  if (MASKED && SEG) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int4 w = *(const int4*)(segk + 32 * kt + 8 * g + 4 * h);
+      sk[4 * g + 0] = w.x; sk[4 * g + 1] = w.y; sk[4 * g + 2] = w.z; sk[4 * g + 3] = w.w;
+    }
+  }
 #pragma unroll
   for (int qt = 0; qt < kQT; ++qt) {
     const int qi = qw + 32 * qt + i32;
@@ -48,7 +58,8 @@ __device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[kQT], const 
         float p = __builtin_amdgcn_exp2f(s[qt][r] * c_scale);
         if (MASKED) {
           const int key = k0 + 32 * kt + acc_row(r, h);
-          p = (key >= N || (causal && key > qi) || (band && qi - key >= band)) ? 0.f : p;
+          p = (key >= N || (causal && key > qi) || (band && qi - key >= band) ||
+               (SEG && sk[r] != sq)) ? 0.f : p;
         }
         dsv[e] = p * dp[qt][r];
       }
@@ -86,12 +97,13 @@ __device__ __forceinline__ void dq_half_scores(const __bf16* ks, const __bf16* v
   }
 }
 
-template <bool MASKED>
+template <bool MASKED, bool SEG>
 __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int lane, int k0,
                                         int qw, int N, float c_scale,
                                         const bf16x8_t (&qop)[kQT][4], const bf16x8_t (&oop)[kQT][4],
                                         const float (&nls)[kQT], const float (&ndl)[kQT],
-                                        floatx16 (&dqacc)[2][kQT], int causal, int band) {
+                                        floatx16 (&dqacc)[2][kQT], int causal, int band,
+                                        const int32_t* segk, int32_t sq) {
   const int i32 = lane & 31, h = lane >> 5;
   floatx16 s0[kQT], dp0[kQT], s1[kQT], dp1[kQT];
   uint32_t dsp0[kQT][8], dsp1[kQT][8];
@@ -102,7 +114,8 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) ktr0[half][dt] = read_tr(ks, lane, half, 32 * dt);
   dq_half_scores(ks, vs, 1, i32, h, qop, oop, nls, ndl, s1, dp1);
-  dq_half_softmax<MASKED>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale, causal, band);
+  dq_half_softmax<MASKED, SEG>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale, causal, band,
+                               segk, sq);
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -114,7 +127,8 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt)
         dqacc[dt][qt] = mma(ktr0[half][dt], chunk_op(dsp0[qt], half), dqacc[dt][qt]);
-  dq_half_softmax<MASKED>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale, causal, band);
+  dq_half_softmax<MASKED, SEG>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale, causal, band,
+                               segk, sq);
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -129,16 +143,19 @@ struct alignas(16) KVStage {
   __bf16 v[kT2 * kD];
 };
 
-// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does.
-template <bool CAUSAL, bool BANDED>
+// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does;
+// SEG: only pairs of equal segment ids (seg, [B][N], batch = head / hpb) exist.
+template <bool CAUSAL, bool BANDED, bool SEG>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ dout, const float* __restrict__ nlseg,
     const float* __restrict__ ndeltag, __bf16* __restrict__ dq, int heads, int N, int nqb,
-    float c_scale, float scale, int band_arg) {
+    float c_scale, float scale, int band_arg, const int32_t* __restrict__ seg, int hpb) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
+  __shared__ __attribute__((aligned(16))) int32_t sg[3][SEG ? kT2 : 4];  // the stages' key ids
+  static_assert(kQT == 1 && kT2 == kT, "one query column per wave, one tile per stage");
   int head, qb;
   if (!map_block(blockIdx.x, heads, nqb, true, 4, head, qb)) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -167,6 +184,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
     nls[qt] = qi < N ? nlseg[(size_t)head * N + qi] : 0.f;
     ndl[qt] = qi < N ? ndeltag[(size_t)head * N + qi] : 0.f;
   }
+  // segment ids: the lane's query id and the range of the wave's valid ids
+  const int32_t* segrow = SEG ? seg + (size_t)(head / hpb) * N : nullptr;
+  int32_t sq = 0, sqlo = 0, sqhi = 0;
+  if (SEG) {
+    const int qi = qw + i32;
+    sq = qi < N ? segrow[qi] : 0;
+    sqlo = qi < N ? sq : INT32_MAX;
+    sqhi = qi < N ? sq : INT32_MIN;
+#pragma unroll
+    for (int o2 = 16; o2 >= 1; o2 >>= 1) {
+      sqlo = min(sqlo, __shfl_xor(sqlo, o2));
+      sqhi = max(sqhi, __shfl_xor(sqhi, o2));
+    }
+    sqlo = __builtin_amdgcn_readfirstlane(sqlo);
+    sqhi = __builtin_amdgcn_readfirstlane(sqhi);
+  }
   floatx16 dqacc[2][kQT];  // [dt][qt]: (feature x query), lane holds a query column
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -180,37 +213,51 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
   const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
   const uint32_t tbytes = (uint32_t)N * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);
-  auto issue = [&](KVStage& s, int t) {
+  __amdgpu_buffer_rsrc_t rs = rk;
+  if (SEG) rs = head_rsrc(segrow, (uint32_t)N * 4);
+  // wave 0 also copies the tile's key ids (one more load per tile; the barrier
+  // waits still leave only the newest tile's loads in flight)
+  auto issue = [&](KVStage& s, int32_t* sgs, int t) {
     tile_async<kT2, kWaves>(rk, s.k, t * kT2, wave, lane);
     tile_async<kT2, kWaves>(rv, s.v, t * kT2, wave, lane);
+    if (SEG && wave == 0) rows_async(rs, (float*)sgs, t * kT2, lane);
   };
-  auto step = [&](KVStage& cur, KVStage& ahead, int t) {
+  auto step = [&](KVStage& cur, int32_t* sgc, KVStage& ahead, int32_t* sga, int t) {
     const bool pre = t + 2 < ntiles;
-    if (pre) issue(ahead, t + 2);
-#pragma unroll
-    for (int sub = 0; sub < kT2 / kT; ++sub) {
-      const int k0 = t * kT2 + sub * kT;
-      if (k0 <= whi && k0 + kT - 1 >= wlo) {
+    if (pre) issue(ahead, sga, t + 2);
+    const int k0 = t * kT2;
+    if (k0 <= whi && k0 + kT - 1 >= wlo) {
+      // segments: no key id in the wave's id range -> no pair; all ids one and
+      // the same -> the ids mask nothing
+      bool seg_some = true, seg_one = true;
+      if (SEG) {
+        const int32_t skey = sgc[lane];
+        const bool kin = k0 + lane < N;
+        seg_some = __any(kin && skey >= sqlo && skey <= sqhi);
+        seg_one = sqlo == sqhi && __all(!kin || skey == sqlo);
+      }
+      if (seg_some) {
         // masked: some pair of the tile is absent for some query of the wave
-        if ((causal && k0 + kT - 1 > qw) || (k0 + kT > N) || (band && k0 < qw + kRowsW - band))
-          dq_tile<true>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale,
-                        qop, oop, nls, ndl, dqacc, causal, band);
+        if ((causal && k0 + kT - 1 > qw) || (k0 + kT > N) || (band && k0 < qw + kRowsW - band) ||
+            !seg_one)
+          dq_tile<true, SEG>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc,
+                             causal, band, sgc, sq);
         else
-          dq_tile<false>(cur.k + sub * kT * kD, cur.v + sub * kT * kD, lane, k0, qw, N, c_scale,
-                         qop, oop, nls, ndl, dqacc, causal, band);
+          dq_tile<false, SEG>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc,
+                              causal, band, sgc, sq);
       }
     }
     if (pre) wait_vm_barrier<2 * kT2 / (8 * kWaves)>();
     else wait_vm_barrier<0>();
   };
 
-  issue(st0, t0);
-  if (t0 + 1 < ntiles) issue(st1, t0 + 1);
+  issue(st0, sg[0], t0);
+  if (t0 + 1 < ntiles) issue(st1, sg[1], t0 + 1);
   wait_vm_barrier<0>();
   for (int t = t0; t < ntiles; t += 3) {
-    step(st0, st2, t);
-    if (t + 1 < ntiles) step(st1, st0, t + 1);
-    if (t + 2 < ntiles) step(st2, st1, t + 2);
+    step(st0, sg[0], st2, sg[2], t);
+    if (t + 1 < ntiles) step(st1, sg[1], st0, sg[0], t + 1);
+    if (t + 2 < ntiles) step(st2, sg[2], st1, sg[1], t + 2);
   }
 
 #pragma unroll
@@ -240,11 +287,14 @@ hipError_t launch_bwd_dq_bf16(const __bf16* q, const __bf16* k, const __bf16* v,
   const int nb = (int)((N + kBlk - 1) / kBlk);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nb);
   if (hipError_t e = mark(tm.start[kTimerBwdDq], stream)) return e;
-  auto kern = mk.band > 0 ? bwd_dq_bf16<true, true>
-              : mk.causal ? bwd_dq_bf16<true, false>
-                          : bwd_dq_bf16<false, false>;
+  auto kern = mk.seg ? (mk.band > 0 ? bwd_dq_bf16<true, true, true>
+                        : mk.causal ? bwd_dq_bf16<true, false, true>
+                                    : bwd_dq_bf16<false, false, true>)
+                     : (mk.band > 0 ? bwd_dq_bf16<true, true, false>
+                        : mk.causal ? bwd_dq_bf16<true, false, false>
+                                    : bwd_dq_bf16<false, false, false>);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, dout, nlse, ndelta, dq,
-                     (int)heads, (int)N, nb, c, (float)scale, mk.band);
+                     (int)heads, (int)N, nb, c, (float)scale, mk.band, mk.seg, mk.hpb);
   if (hipError_t e = mark(tm.stop[kTimerBwdDq], stream)) return e;
   return hipGetLastError();
 }

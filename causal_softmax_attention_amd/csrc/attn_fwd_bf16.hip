@@ -107,12 +107,14 @@ __device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][kQT], float 
 
 // One key tile for one wave (32 queries x 64 keys).  MASKED: the tile crosses
 // the wave's diagonal or the end of the sequence.
-template <bool MASKED>
+// SEG: segment ids apply; segk holds the tile's 64 key ids (LDS) and sq the
+// lane's query id, and a pair of different ids is absent.
+template <bool MASKED, bool SEG>
 __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __bf16* pscr,
                                          int lane, int k0, int qw, int N, float c_scale,
                                          int causal, int band, const bf16x8_t (&qop)[kQT][4],
                                          floatx16 (&oacc)[2][kQT], float (&mref)[kQT],
-                                         float (&lsum)[kQT]) {
+                                         float (&lsum)[kQT], const int32_t* segk, int32_t sq) {
   const int i32 = lane & 31, h = lane >> 5;
   // ---- S^T = K Q^T: s[kt][qt] holds keys k0 + 32 kt + acc_row(r, h), query column
   floatx16 s[2][kQT];
@@ -135,10 +137,19 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt) {
         const int qi = qw + 32 * qt + i32;
+        int32_t sk[16];  // ids of the lane's 16 keys of this half (rows acc_row(r, h))
+        if (SEG) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int4 w = *(const int4*)(segk + 32 * kt + 8 * g + 4 * h);
+            sk[4 * g + 0] = w.x; sk[4 * g + 1] = w.y; sk[4 * g + 2] = w.z; sk[4 * g + 3] = w.w;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + 32 * kt + acc_row(r, h);
-          s[kt][qt][r] = absent(qi, j, N, causal, band) ? -__builtin_inff() : s[kt][qt][r];
+          const bool gone = absent(qi, j, N, causal, band) || (SEG && sk[r] != sq);
+          s[kt][qt][r] = gone ? -__builtin_inff() : s[kt][qt][r];
         }
       }
   }
@@ -213,7 +224,7 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
           for (int jj = 0; jj < 16; ++jj) {
             const int j = k0 + 32 * kt + 16 * c16 + jj;
             const float pj = (float)pscr[i32 * 16 + jj];
-            if (absent(qi, j, N, causal, band)) continue;
+            if (absent(qi, j, N, causal, band) || (SEG && segk[j - k0] != sq)) continue;
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -226,16 +237,20 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
   }
 }
 
-// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does.
-template <bool CAUSAL, bool BANDED>
+// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does;
+// SEG: only pairs of equal segment ids (seg, [B][N], batch = head / hpb) exist.
+template <bool CAUSAL, bool BANDED, bool SEG>
 __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale,
-    int band_arg, float* __restrict__ ndelta, float* __restrict__ nlse, float inv_scale) {
+    int band_arg, float* __restrict__ ndelta, float* __restrict__ nlse, float inv_scale,
+    const int32_t* __restrict__ seg, int hpb) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
   __shared__ __bf16 pscr[kWaves][32 * 16];
+  __shared__ __attribute__((aligned(16))) int32_t sg[3][SEG ? kBc : 4];  // the stages' key ids
+  static_assert(kQT == 1, "one query column per wave");
   int head, qb;
   if (!map_block(blockIdx.x, heads, nqb, true, 8, head, qb)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -266,6 +281,23 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < kQT; ++b) oacc[a][b] = floatx16{};
+  // segment ids: the lane's query id, and the range of the wave's valid ids
+  // (a tile none of whose key ids falls in it has no pair for this wave)
+  const int32_t* segrow = SEG ? seg + (size_t)(head / hpb) * N : nullptr;
+  int32_t sq = 0, sqlo = 0, sqhi = 0;
+  if (SEG) {
+    const int qi = qw + i32;
+    sq = qi < N ? segrow[qi] : 0;
+    sqlo = qi < N ? sq : INT32_MAX;
+    sqhi = qi < N ? sq : INT32_MIN;
+#pragma unroll
+    for (int o2 = 16; o2 >= 1; o2 >>= 1) {
+      sqlo = min(sqlo, __shfl_xor(sqlo, o2));
+      sqhi = max(sqhi, __shfl_xor(sqhi, o2));
+    }
+    sqlo = __builtin_amdgcn_readfirstlane(sqlo);
+    sqhi = __builtin_amdgcn_readfirstlane(sqhi);
+  }
   // reference exponents start finite, so a tile whose pairs are all absent for
   // a lane gives it weights exp2(-inf) = 0, and its first present pair takes the
   // exact path (the weight overflows against kRefInit)
@@ -278,34 +310,52 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
 
   const uint32_t tbytes = (uint32_t)N * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);
-  auto issue = [&](KVStage& s, int t) {
+  __amdgpu_buffer_rsrc_t rs = rk;
+  if (SEG) rs = head_rsrc(segrow, (uint32_t)N * 4);
+  // wave 0 also copies the tile's key ids (one 4-byte load per lane); with its
+  // one extra load per tile, the barrier waits below (at most the newest
+  // tile's 4 loads in flight) still cover every older tile
+  auto issue = [&](KVStage& s, int32_t* sgs, int t) {
     tile_async<kBc, kWaves>(rk, s.k, t * kBc, wave, lane);
     tile_async<kBc, kWaves>(rv, s.v, t * kBc, wave, lane);
+    if (SEG && wave == 0) rows_async(rs, (float*)sgs, t * kBc, lane);
   };
-  auto step = [&](KVStage& cur, KVStage& ahead, int t) {
+  auto step = [&](KVStage& cur, int32_t* sgc, KVStage& ahead, int32_t* sga, int t) {
     const bool pre = t + 2 < ntiles;
-    if (pre) issue(ahead, t + 2);
+    if (pre) issue(ahead, sga, t + 2);
     const int k0 = t * kBc;
     if (k0 <= whi && k0 + kBc - 1 >= wlo) {
-      // masked: some pair of the tile is absent for some query of the wave
-      if ((causal && k0 + kBc - 1 > qw) || (k0 + kBc > N) || (band && k0 < qw + kQW - band))
-        fwd_tile<true>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band, qop,
-                       oacc, mref, lsum);
-      else
-        fwd_tile<false>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band, qop,
-                        oacc, mref, lsum);
+      // segments: no key id in the wave's id range -> no pair; all ids one and
+      // the same -> the ids mask nothing (keys past N are masked anyway)
+      bool seg_some = true, seg_one = true;
+      if (SEG) {
+        const int32_t skey = sgc[lane];  // key k0 + lane
+        const bool kin = k0 + lane < N;
+        seg_some = __any(kin && skey >= sqlo && skey <= sqhi);
+        seg_one = sqlo == sqhi && __all(!kin || skey == sqlo);
+      }
+      if (seg_some) {
+        // masked: some pair of the tile is absent for some query of the wave
+        if ((causal && k0 + kBc - 1 > qw) || (k0 + kBc > N) || (band && k0 < qw + kQW - band) ||
+            !seg_one)
+          fwd_tile<true, SEG>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band,
+                              qop, oacc, mref, lsum, sgc, sq);
+        else
+          fwd_tile<false, SEG>(cur.k, cur.v, pscr[wave], lane, k0, qw, N, c_scale, causal, band,
+                               qop, oacc, mref, lsum, sgc, sq);
+      }
     }
     if (pre) wait_vm_barrier<2 * kBc / (8 * kWaves)>();
     else wait_vm_barrier<0>();
   };
 
-  issue(st0, t0);
-  if (t0 + 1 < ntiles) issue(st1, t0 + 1);
+  issue(st0, sg[0], t0);
+  if (t0 + 1 < ntiles) issue(st1, sg[1], t0 + 1);
   wait_vm_barrier<0>();
   for (int t = t0; t < ntiles; t += 3) {
-    step(st0, st2, t);
-    if (t + 1 < ntiles) step(st1, st0, t + 1);
-    if (t + 2 < ntiles) step(st2, st1, t + 2);
+    step(st0, sg[0], st2, sg[2], t);
+    if (t + 1 < ntiles) step(st1, sg[1], st0, sg[0], t + 1);
+    if (t + 2 < ntiles) step(st2, sg[2], st1, sg[1], t + 2);
   }
 
   // ---- epilogue: l over both lane halves, O = O^T / l, lse = (m + log2 l) ln 2.
@@ -354,15 +404,19 @@ hipError_t launch_fwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, __
   const int nqb = (int)((N + kBr - 1) / kBr);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nqb);
   const float c = (float)(scale * 1.4426950408889634);  // scale * log2(e)
-  auto kern = mk.band > 0 ? attn_fwd_bf16_kernel<true, true>
-              : mk.causal ? attn_fwd_bf16_kernel<true, false>
-                          : attn_fwd_bf16_kernel<false, false>;
+  auto kern = mk.seg ? (mk.band > 0 ? attn_fwd_bf16_kernel<true, true, true>
+                        : mk.causal ? attn_fwd_bf16_kernel<true, false, true>
+                                    : attn_fwd_bf16_kernel<false, false, true>)
+                     : (mk.band > 0 ? attn_fwd_bf16_kernel<true, true, false>
+                        : mk.causal ? attn_fwd_bf16_kernel<true, false, false>
+                                    : attn_fwd_bf16_kernel<false, false, false>);
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
   // the backward workspace: -delta per row, then -lse / scale per row
   float* ndelta = (float*)bwd_ws;
   float* nlse = ndelta ? ndelta + heads * N : nullptr;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, (int)heads,
-                     (int)N, nqb, c, mk.band, ndelta, nlse, (float)(1.0 / scale));
+                     (int)N, nqb, c, mk.band, ndelta, nlse, (float)(1.0 / scale), mk.seg,
+                     mk.hpb);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }

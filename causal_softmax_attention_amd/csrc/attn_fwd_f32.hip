@@ -50,10 +50,11 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 constexpr int kLd = 68;
 __device__ __forceinline__ int at32(int row, int col) { return row * kLd + col; }
 
-struct Smem {
+struct alignas(16) Smem {
   float k[2][kBc * kLd];       // [key][feature]
   float vt[2][kD * kLd];       // [feature][key]
   float p[kWaves][kQW * kBc];  // select path: the wave's weights as [query][key]
+  int32_t seg[2][kBc];         // segment ids of the tile's keys (when they apply)
 };
 
 __device__ __forceinline__ bool finite4(float4 x) {
@@ -67,12 +68,14 @@ __device__ __forceinline__ bool absent(int i, int j, int N, int causal, int band
   return j >= N || (causal && j > i) || (band && i - j >= band);
 }
 
-template <bool MASKED>
+// SEG: segment ids apply (segk: the tile's key ids, sq: the lane's query id).
+template <bool MASKED, bool SEG>
 __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, float* pscr,
                                              int lane, int k0, int qw, int N, float c_scale,
                                              int causal, int band, bool vnonfinite,
                                              const float (&qreg)[32], floatx16 (&oacc)[2],
-                                             float& mref, float& lsum) {
+                                             float& mref, float& lsum, const int32_t* segk,
+                                             int32_t sq) {
   const int i32 = lane & 31, h = lane >> 5;
   const int qi = qw + i32;
   floatx16 s[2];  // [kt]: scores, then (in place) weights
@@ -92,12 +95,22 @@ __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, f
     }
     if (MASKED) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+        int32_t sk[16];  // ids of the lane's 16 keys of this half
+        if (SEG) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int4 w = *(const int4*)(segk + 32 * kt + 8 * g + 4 * h);
+            sk[4 * g + 0] = w.x; sk[4 * g + 1] = w.y; sk[4 * g + 2] = w.z; sk[4 * g + 3] = w.w;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = k0 + 32 * kt + acc_row(r, h);
-          s[kt][r] = absent(qi, j, N, causal, band) ? -__builtin_inff() : s[kt][r];
+          const bool gone = absent(qi, j, N, causal, band) || (SEG && sk[r] != sq);
+          s[kt][r] = gone ? -__builtin_inff() : s[kt][r];
         }
+      }
     }
   };
   float part = 0.f;
@@ -161,7 +174,7 @@ __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, f
     for (int jj = 0; jj < kBc; ++jj) {
       const int j = k0 + jj;
       const float pj = pscr[i32 * kBc + jj];
-      if (absent(qi, j, N, causal, band)) continue;
+      if (absent(qi, j, N, causal, band) || (SEG && segk[jj] != sq)) continue;
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
@@ -172,12 +185,13 @@ __device__ __forceinline__ void fwd_tile_f32(const float* ks, const float* vt, f
   }
 }
 
-// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does.
-template <bool CAUSAL, bool BANDED>
+// CAUSAL: the causal predicate applies; BANDED: a window of band_arg keys does;
+// SEG: only pairs of equal segment ids (seg, [B][N], batch = head / hpb) exist.
+template <bool CAUSAL, bool BANDED, bool SEG>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ o, float* __restrict__ lse, int heads, int N, int nqb, float c_scale,
-    int band_arg, float* __restrict__ delta) {
+    int band_arg, float* __restrict__ delta, const int32_t* __restrict__ seg, int hpb) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
   __shared__ Smem sm;
@@ -188,6 +202,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
   const size_t base = (size_t)head * N * kD;
   const int qw = qb * kBr + wave * kQW;
   const int wq_last = min(qw + kQW, N) - 1;
+  // segment ids: the lane's query id and the range of the wave's valid ids
+  const int32_t* segrow = SEG ? seg + (size_t)(head / hpb) * N : nullptr;
+  int32_t sq = 0, sqlo = 0, sqhi = 0, sreg = 0;
+  if (SEG) {
+    const int qi0 = qw + i32;
+    sq = qi0 < N ? segrow[qi0] : 0;
+    sqlo = qi0 < N ? sq : INT32_MAX;
+    sqhi = qi0 < N ? sq : INT32_MIN;
+#pragma unroll
+    for (int o2 = 16; o2 >= 1; o2 >>= 1) {
+      sqlo = min(sqlo, __shfl_xor(sqlo, o2));
+      sqhi = max(sqhi, __shfl_xor(sqhi, o2));
+    }
+  }
   // keys of the workgroup's queries: from its first query's window start to
   // its last query (causal) or the end (full)
   const int t0 = band ? max(0, qb * kBr - band + 1) / kBc : 0;
@@ -228,6 +256,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
       if (jk < N) kreg[u] = *(const float4*)(k + base + (size_t)jk * kD + 4 * (c & 15));
       if (jv < N) vreg[u] = *(const float4*)(v + base + (size_t)jv * kD + 4 * (c >> 6));
     }
+    if (SEG && tid < kBc) sreg = t * kBc + tid < N ? segrow[t * kBc + tid] : 0;
   };
   auto store_tile = [&](int buf) {
     bool fin = true;
@@ -241,6 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
       sm.vt[buf][at32(d + 3, key)] = vreg[u].w;
       fin &= finite4(vreg[u]);
     }
+    if (SEG && tid < kBc) sm.seg[buf][tid] = sreg;
     return fin;
   };
 
@@ -253,13 +283,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
     if (more) load_tile(t + 1);
     const int k0 = t * kBc;
     if (active && k0 <= whi && k0 + kBc - 1 >= wlo) {
+      // segments: no key id in the wave's id range -> no pair; all ids one and
+      // the same -> the ids mask nothing (keys past N are masked anyway)
+      bool seg_some = true, seg_one = true;
+      if (SEG) {
+        const int32_t skey = sm.seg[buf][lane];
+        const bool kin = k0 + lane < N;
+        seg_some = __any(kin && skey >= sqlo && skey <= sqhi);
+        seg_one = sqlo == sqhi && __all(!kin || skey == sqlo);
+      }
       // masked: some pair of the tile is absent for some query of the wave
-      if ((causal && k0 + kBc - 1 > qw) || (k0 + kBc > N) || (band && k0 < qw + kQW - band))
-        fwd_tile_f32<true>(sm.k[buf], sm.vt[buf], sm.p[wave], lane, k0, qw, N, c_scale, causal,
-                           band, vnonfinite != 0, qreg, oacc, mref, lsum);
-      else
-        fwd_tile_f32<false>(sm.k[buf], sm.vt[buf], sm.p[wave], lane, k0, qw, N, c_scale, causal,
-                            band, false, qreg, oacc, mref, lsum);
+      if (!seg_some) {
+      } else if ((causal && k0 + kBc - 1 > qw) || (k0 + kBc > N) ||
+                 (band && k0 < qw + kQW - band) || !seg_one) {
+        fwd_tile_f32<true, SEG>(sm.k[buf], sm.vt[buf], sm.p[wave], lane, k0, qw, N, c_scale,
+                                causal, band, vnonfinite != 0, qreg, oacc, mref, lsum,
+                                sm.seg[buf], sq);
+      } else {
+        fwd_tile_f32<false, SEG>(sm.k[buf], sm.vt[buf], sm.p[wave], lane, k0, qw, N, c_scale,
+                                 causal, band, false, qreg, oacc, mref, lsum, sm.seg[buf], sq);
+      }
     }
     const bool fin = more ? store_tile(buf ^ 1) : true;
     vnonfinite = __syncthreads_or(!fin);
@@ -297,12 +340,15 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   const int nqb = (int)((N + kBr - 1) / kBr);
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nqb);
   const float c = (float)(scale * 1.4426950408889634);
-  auto kern = mk.band > 0 ? attn_fwd_f32_kernel<true, true>
-              : mk.causal ? attn_fwd_f32_kernel<true, false>
-                          : attn_fwd_f32_kernel<false, false>;
+  auto kern = mk.seg ? (mk.band > 0 ? attn_fwd_f32_kernel<true, true, true>
+                        : mk.causal ? attn_fwd_f32_kernel<true, false, true>
+                                    : attn_fwd_f32_kernel<false, false, true>)
+                     : (mk.band > 0 ? attn_fwd_f32_kernel<true, true, false>
+                        : mk.causal ? attn_fwd_f32_kernel<true, false, false>
+                                    : attn_fwd_f32_kernel<false, false, false>);
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, stream, q, k, v, o, lse, (int)heads,
-                     (int)N, nqb, c, mk.band, (float*)bwd_ws);
+                     (int)N, nqb, c, mk.band, (float*)bwd_ws, mk.seg, mk.hpb);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }

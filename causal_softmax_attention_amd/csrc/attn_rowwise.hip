@@ -66,20 +66,31 @@ __device__ __forceinline__ void load_tiles(A (*xs)[kD], A (*ys)[kD], const T* x,
   }
 }
 
+// Segment ids of rows [r0, r0 + kTile) into LDS (nothing without ids).
+__device__ __forceinline__ void load_segs(int32_t* segs, const int32_t* segrow, int r0, int N) {
+  if (segrow && threadIdx.x < kTile) {
+    const int j = r0 + (int)threadIdx.x;
+    segs[threadIdx.x] = j < N ? segrow[j] : 0;
+  }
+}
+
 template <typename T, int S>
 __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
                                                      const T* __restrict__ k,
                                                      const T* __restrict__ v, T* __restrict__ o,
                                                      acc_t<T>* __restrict__ lse, int N, int nqb,
                                                      acc_t<T> scale, int causal, int band,
-                                                     acc_t<T>* __restrict__ delta) {
+                                                     acc_t<T>* __restrict__ delta,
+                                                     const int32_t* __restrict__ seg, int hpb) {
   using A = acc_t<T>;
   constexpr int kRows = Split<S>::kRows;
   __shared__ A ks[kTile][kD];
   __shared__ A vs[kTile][kD];
+  __shared__ int32_t segs[kTile];
   const int head = blockIdx.x / nqb;
   const int qb = nqb - 1 - (blockIdx.x % nqb);  // longest rows first
   const size_t base = (size_t)head * N * kD;
+  const int32_t* segrow = seg ? seg + (size_t)(head / hpb) * N : nullptr;
   const int g = threadIdx.x % kG, f0 = kF * g;
   const int grp = threadIdx.x / kG, r = grp / S, sp = grp % S;  // row r of the block, split sp
   const int i = qb * kRows + r;
@@ -93,18 +104,20 @@ __global__ __launch_bounds__(kThr) void fwd_rowwise(const T* __restrict__ q,
     acc[f] = 0;
   }
   A m = neg_inf<A>(), l = 0;
+  const int32_t si = segrow && valid ? segrow[i] : 0;
   // keys of the block's rows: from its first row's window start to its last row
   const int kbeg = band ? max(0, qb * kRows - band + 1) / kTile * kTile : 0;
   const int kend = causal ? min(N, (qb + 1) * kRows) : N;
   for (int k0 = kbeg; k0 < kend; k0 += kTile) {
     __syncthreads();
     load_tiles(ks, vs, k, v, base, k0, N);
+    load_segs(segs, segrow, k0, N);
     __syncthreads();
     const int jn = min(kTile, kend - k0);
     for (int jj = sp; jj < jn; jj += S) {
       const int j = k0 + jj;
       if (j > jhi) break;  // absent pairs past the row (the whole group leaves together)
-      if (j < jlo) continue;
+      if (j < jlo || (segrow && segs[jj] != si)) continue;
       A s = 0;
 #pragma unroll
       for (int f = 0; f < kF; ++f) s += qr[f] * ks[jj][f0 + f];
@@ -189,13 +202,15 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
     const acc_t<T>* __restrict__ delta, T* __restrict__ dk, T* __restrict__ dv, int N, int nkb,
-    acc_t<T> scale, int causal, int band) {
+    acc_t<T> scale, int causal, int band, const int32_t* __restrict__ seg, int hpb) {
   using A = acc_t<T>;
   constexpr int kRows = Split<S>::kRows;
   __shared__ A qs[kTile][kD];
   __shared__ A dos[kTile][kD];
   __shared__ A ls[kTile], ds_[kTile];
+  __shared__ int32_t segs[kTile];
   const int head = blockIdx.x / nkb;
+  const int32_t* segrow = seg ? seg + (size_t)(head / hpb) * N : nullptr;
   const int kb = blockIdx.x % nkb;  // low key blocks see the most queries: they come first
   const size_t base = (size_t)head * N * kD;
   const int g = threadIdx.x % kG, f0 = kF * g;
@@ -203,6 +218,7 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
   const int j = kb * kRows + r;
   const bool valid = j < N;
   const int ilo = causal ? j : 0, ihi = band ? j + band - 1 : N - 1;  // this key's queries
+  const int32_t sj = segrow && valid ? segrow[j] : 0;
   A kr[kF], vr[kF], gk[kF], gv[kF];
 #pragma unroll
   for (int f = 0; f < kF; ++f) {
@@ -216,6 +232,7 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
   for (int q0 = qbeg; q0 < qend; q0 += kTile) {
     __syncthreads();
     load_tiles(qs, dos, q, dout, base, q0, N);
+    load_segs(segs, segrow, q0, N);
     if (threadIdx.x < kTile) {
       const int i = q0 + threadIdx.x;
       ls[threadIdx.x] = i < N ? lse[(size_t)head * N + i] : A(0);
@@ -224,7 +241,7 @@ __global__ __launch_bounds__(kThr) void bwd_dkdv_rowwise(
     __syncthreads();
     const int in = min(kTile, qend - q0);
     for (int ii = sp; ii < in; ii += S) {
-      if (q0 + ii < ilo || q0 + ii > ihi) continue;  // pair (i, j) absent
+      if (q0 + ii < ilo || q0 + ii > ihi || (segrow && segs[ii] != sj)) continue;  // absent
       A s = 0, dp = 0;
 #pragma unroll
       for (int f = 0; f < kF; ++f) {
@@ -276,12 +293,14 @@ __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const acc_t<T>* __restrict__ lse,
     const acc_t<T>* __restrict__ delta, T* __restrict__ dq, int N, int nqb, acc_t<T> scale,
-    int causal, int band) {
+    int causal, int band, const int32_t* __restrict__ seg, int hpb) {
   using A = acc_t<T>;
   constexpr int kRows = Split<S>::kRows;
   __shared__ A ks[kTile][kD];
   __shared__ A vs[kTile][kD];
+  __shared__ int32_t segs[kTile];
   const int head = blockIdx.x / nqb;
+  const int32_t* segrow = seg ? seg + (size_t)(head / hpb) * N : nullptr;
   const int qb = nqb - 1 - (blockIdx.x % nqb);
   const size_t base = (size_t)head * N * kD;
   const int g = threadIdx.x % kG, f0 = kF * g;
@@ -297,18 +316,20 @@ __global__ __launch_bounds__(kThr) void bwd_dq_rowwise(
   }
   const A li = valid ? lse[(size_t)head * N + i] : A(0);
   const A di = valid ? delta[(size_t)head * N + i] : A(0);
+  const int32_t si = segrow && valid ? segrow[i] : 0;
   const int jlo = band ? i - band + 1 : 0, jhi = causal ? i : N - 1;
   const int kbeg = band ? max(0, qb * kRows - band + 1) / kTile * kTile : 0;
   const int kend = causal ? min(N, (qb + 1) * kRows) : N;
   for (int k0 = kbeg; k0 < kend; k0 += kTile) {
     __syncthreads();
     load_tiles(ks, vs, k, v, base, k0, N);
+    load_segs(segs, segrow, k0, N);
     __syncthreads();
     const int jn = min(kTile, kend - k0);
     for (int jj = sp; jj < jn; jj += S) {
       const int j = k0 + jj;
       if (j > jhi) break;
-      if (j < jlo) continue;
+      if (j < jlo || (segrow && segs[jj] != si)) continue;
       A s = 0, dp = 0;
 #pragma unroll
       for (int f = 0; f < kF; ++f) {
@@ -354,7 +375,8 @@ hipError_t launch_fwd(const T* q, const T* k, const T* v, T* o, void* lse, int64
   auto kern = sp == 32 ? fwd_rowwise<T, 32> : sp == 8 ? fwd_rowwise<T, 8> : fwd_rowwise<T, 1>;
   if (hipError_t e = mark(tm.start[kTimerFwd], stream)) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)(heads * nqb)), dim3(kThr), 0, stream, q, k, v, o,
-                     (A*)lse, (int)N, nqb, (A)scale, mk.causal, mk.band, (A*)bwd_ws);
+                     (A*)lse, (int)N, nqb, (A)scale, mk.causal, mk.band, (A*)bwd_ws, mk.seg,
+                     mk.hpb);
   if (hipError_t e = mark(tm.stop[kTimerFwd], stream)) return e;
   return hipGetLastError();
 }
@@ -386,11 +408,13 @@ hipError_t launch_bwd(const T* q, const T* k, const T* v, const T* o, const T* d
   auto kdq = sp == 32 ? bwd_dq_rowwise<T, 32> : sp == 8 ? bwd_dq_rowwise<T, 8> : bwd_dq_rowwise<T, 1>;
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
   hipLaunchKernelGGL(kdkdv, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q, k, v, dout,
-                     (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale, mk.causal, mk.band);
+                     (const A*)lse, delta, dk, dv, (int)N, nb, (A)scale, mk.causal, mk.band,
+                     mk.seg, mk.hpb);
   if (hipError_t e = mark(tm.stop[kTimerBwdDkdv], stream)) return e;
   if (hipError_t e = mark(tm.start[kTimerBwdDq], stream)) return e;
   hipLaunchKernelGGL(kdq, dim3((unsigned)(heads * nb)), dim3(kThr), 0, stream, q, k, v, dout,
-                     (const A*)lse, delta, dq, (int)N, nb, (A)scale, mk.causal, mk.band);
+                     (const A*)lse, delta, dq, (int)N, nb, (A)scale, mk.causal, mk.band, mk.seg,
+                     mk.hpb);
   if (hipError_t e = mark(tm.stop[kTimerBwdDq], stream)) return e;
   return hipGetLastError();
 }

@@ -27,13 +27,17 @@ enum {
 inline hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
 
 // Which (query i, key j) pairs exist (the join predicate): j < N and
-//   causal != 0: j <= i;   band > 0: i - j < band   (band 0: no lower limit).
+//   causal != 0: j <= i;   band > 0: i - j < band   (band 0: no lower limit);
+//   seg non-null: seg[b][i] == seg[b][j], where head h of the launch belongs to
+//   batch b = h / hpb and seg is [B][N] int32 (segment ids of the tokens).
 // causal = 1, band = 0 is the causal view; causal = 0, band = 0 every pair;
 // causal = 1, band = w a causal window of w keys.  (causal = 0 with band > 0
 // is not used.)
 struct Mask {
   int causal = 1;
   int band = 0;
+  const int32_t* seg = nullptr;
+  int hpb = 1;  // heads per batch (the H of [B, H, N, D])
 };
 
 // Every forward launcher takes `bwd_ws`: null, or the backward workspace, which

@@ -109,6 +109,30 @@ def workload(name: str) -> AttentionInputs:
     return attention_inputs(seed, B, H, N, dtype, mult)
 
 
+def segment_ids(seed: int, B: int, N: int, kind: str = "packed", mean_len: int = 512,
+                n_ids: int = 3) -> np.ndarray:
+    """Segment ids int32 [B, N] from ``default_rng(seed)``.
+
+    "packed": documents packed back to back, one id per document (0, 1, 2, ...
+    along the row), lengths drawn from a geometric law of mean ``mean_len``
+    (at least 1 token), a mix of short and long documents.
+    "interleaved": every token an id drawn uniformly from ``n_ids`` values, so
+    equal ids are scattered (no key tile is one segment).
+    """
+    rng = np.random.default_rng(seed)
+    if kind == "interleaved":
+        return rng.integers(0, n_ids, size=(B, N)).astype(np.int32)
+    if kind != "packed":
+        raise ValueError(f"unknown segment kind {kind!r}")
+    out = np.empty((B, N), dtype=np.int32)
+    for b in range(B):
+        lens = []
+        while sum(lens) < N:
+            lens.append(int(rng.geometric(1.0 / mean_len)))
+        out[b] = np.repeat(np.arange(len(lens), dtype=np.int32), lens)[:N]
+    return out
+
+
 def page_sizes_inputs() -> dict[int, tuple[np.ndarray, np.ndarray, np.ndarray]]:
     """The demo's forward/gradient sizes: one rng (seed 0) drawn for n = 64, then n = 256."""
     rng = np.random.default_rng(0)

@@ -154,6 +154,31 @@ ATTN_API int attn_bwd(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64
                       const void* o, const void* dout, const void* lse, void* dq, void* dk,
                       void* dv, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Segment predicate: attn_fwd / attn_bwd with one more condition on the
+ * join, equality of a per-token segment id (pages: "Show HN: automatic
+ * deduction of FlashAttention kernel from 25 lines of SQL", the demo script's
+ * claim that its fusion rule covers any softmax-weighted join, and its check
+ * that masks are rows absent from the join).  The pair (i, j) exists when
+ * mask / window admit it AND seg[b][i] == seg[b][j]; so documents packed
+ * into one sequence attend only within themselves.
+ *   seg   device int32 [B, N], 4-byte aligned, shared by the H heads of each
+ *         batch; any values (equal ids need not be contiguous).  Read only;
+ *         no output or workspace may overlap it.
+ *   lse for attn_bwd_seg must come from attn_fwd_seg with the same seg, mask
+ *   and window.  Every row keeps at least the pair (i, i), so no row is empty.
+ * Other arguments, workspace size included, as attn_fwd / attn_bwd.
+ * Returns ATTN_OK / ATTN_EINVAL (also for a null seg) / ATTN_EUNSUPPORTED /
+ * ATTN_EHIP. */
+ATTN_API int attn_fwd_seg(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D,
+                          double scale, attn_mask_t mask, int64_t window, const int32_t* seg,
+                          const void* q, const void* k, const void* v, void* o, void* lse,
+                          void* stream);
+ATTN_API int attn_bwd_seg(attn_dtype_t dtype, int64_t B, int64_t H, int64_t N, int64_t D,
+                          double scale, attn_mask_t mask, int64_t window, const int32_t* seg,
+                          const void* q, const void* k, const void* v, const void* o,
+                          const void* dout, const void* lse, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Training step of the pages' GRADIENT statement (loss = SUM(x * x) / 2 over
  * every output value, so the upstream gradient is dout = o), with the loss
  * fused into the forward:

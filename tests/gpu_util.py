@@ -51,11 +51,16 @@ class Guarded:
                     torch.equal(self.raw[p + n:], self.ref[p + n:]))
 
 
-def run_fwd(q, k, v, scale=0.125, guard=True, mask=None, window=0):
-    """The forward through attn_causal_fwd, or attn_fwd when a mask is named."""
+def run_fwd(q, k, v, scale=0.125, guard=True, mask=None, window=0, seg=None):
+    """The forward through attn_causal_fwd, or attn_fwd when a mask is named,
+    or attn_fwd_seg with segment ids (mask default causal)."""
     B, H, N, D = q.shape
-    call = (lambda **kw: csa.attn_causal_fwd(q, k, v, scale, **kw)) if mask is None else \
-        (lambda **kw: csa.attn_fwd(q, k, v, scale, mask, window, **kw))
+    if seg is not None:
+        call = lambda **kw: csa.attn_fwd_seg(q, k, v, seg, scale, mask or "causal", window, **kw)
+    elif mask is None:
+        call = lambda **kw: csa.attn_causal_fwd(q, k, v, scale, **kw)
+    else:
+        call = lambda **kw: csa.attn_fwd(q, k, v, scale, mask, window, **kw)
     if not guard:
         return call()
     lse_dt = torch.float64 if q.dtype == torch.float64 else torch.float32
@@ -66,11 +71,16 @@ def run_fwd(q, k, v, scale=0.125, guard=True, mask=None, window=0):
     return o, lse
 
 
-def run_bwd(q, k, v, o, dout, lse, scale=0.125, guard=True, mask=None, window=0):
-    """The backward through attn_causal_bwd, or attn_bwd when a mask is named."""
-    call = (lambda **kw: csa.attn_causal_bwd(q, k, v, o, dout, lse, scale, **kw)) \
-        if mask is None else \
-        (lambda **kw: csa.attn_bwd(q, k, v, o, dout, lse, scale, mask, window, **kw))
+def run_bwd(q, k, v, o, dout, lse, scale=0.125, guard=True, mask=None, window=0, seg=None):
+    """The backward through attn_causal_bwd, or attn_bwd when a mask is named,
+    or attn_bwd_seg with segment ids (mask default causal)."""
+    if seg is not None:
+        call = lambda **kw: csa.attn_bwd_seg(q, k, v, o, dout, lse, seg, scale,
+                                             mask or "causal", window, **kw)
+    elif mask is None:
+        call = lambda **kw: csa.attn_causal_bwd(q, k, v, o, dout, lse, scale, **kw)
+    else:
+        call = lambda **kw: csa.attn_bwd(q, k, v, o, dout, lse, scale, mask, window, **kw)
     if not guard:
         return call()
     gs = [Guarded(tuple(q.shape), q.dtype) for _ in range(3)]

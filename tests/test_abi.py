@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
                                          "nw_gauss_average", "attn_set_kernel_timer",
                                          "attn_last_error", "attn_matrix_to_table",
                                          "attn_table_workspace_bytes", "attn_table_to_matrix",
-                                         "attn_qkv_project"])
+                                         "attn_qkv_project", "attn_fwd_seg",
+                                         "attn_bwd_seg"])
 
 
 def test_library_exports_every_declared_symbol(L):
@@ -159,6 +160,53 @@ def test_masked_entry_points_check_sizes_first(L):
         assert mbwd(L, m, 4, scale=0.0) == csa.ATTN_EINVAL
     assert L.attn_bwd_workspace_bytes(2, 2, 3, 100, 64) == \
         L.attn_causal_bwd_workspace_bytes(2, 2, 3, 100, 64)
+
+
+def sfwd(L, seg=0x900000, **kw):
+    a = dict(dtype=2, B=1, H=1, N=16, D=64, scale=0.125, mask=0, window=0,
+             o=0x100000, lse=0x200000)
+    a.update(kw)
+    return L.attn_fwd_seg(a["dtype"], a["B"], a["H"], a["N"], a["D"], a["scale"], a["mask"],
+                          a["window"], ctypes.c_void_p(seg), P, P, P, ctypes.c_void_p(a["o"]),
+                          ctypes.c_void_p(a["lse"]), None)
+
+
+def sbwd(L, seg=0xb00000, **kw):
+    a = dict(dtype=2, B=1, H=1, N=16, D=64, scale=0.125, mask=0, window=0)
+    a.update(kw)
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(10)]
+    if "dq" in kw:
+        p[6] = ctypes.c_void_p(kw["dq"])
+    need = L.attn_bwd_workspace_bytes(2, 1, 1, 16, 64)
+    return L.attn_bwd_seg(a["dtype"], a["B"], a["H"], a["N"], a["D"], a["scale"], a["mask"],
+                          a["window"], ctypes.c_void_p(seg), *p, need, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seg=0), csa.ATTN_EINVAL),                      # null segment ids
+    (dict(seg=0x900002), csa.ATTN_EINVAL),               # not 4-byte aligned
+    (dict(seg=0x100010), csa.ATTN_EINVAL),               # o overlaps the ids
+    (dict(seg=0x200000), csa.ATTN_EINVAL),               # lse overlaps the ids
+    (dict(D=32), csa.ATTN_EUNSUPPORTED),
+    (dict(mask=2, window=0), csa.ATTN_EINVAL),
+    (dict(mask=9), csa.ATTN_EINVAL),
+])
+def test_fwd_seg_rejects(L, kw, code):
+    assert sfwd(L, **kw) == code
+    assert csa.attn_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(seg=0), csa.ATTN_EINVAL),
+    (dict(seg=0xb00001), csa.ATTN_EINVAL),
+    (dict(seg=0x700000), csa.ATTN_EINVAL),               # dq overlaps the ids
+    (dict(seg=0xa00000), csa.ATTN_EINVAL),               # the workspace overlaps the ids
+    (dict(N=0), csa.ATTN_EINVAL),
+    (dict(mask=2, window=-1), csa.ATTN_EINVAL),
+])
+def test_bwd_seg_rejects(L, kw, code):
+    assert sbwd(L, **kw) == code
+    assert csa.attn_last_error() != ""
 
 
 def train_fwd(L, ws_bytes=None, loss=0x900000, ws=0x800000, **kw):
@@ -388,6 +436,22 @@ def test_binding_rejects_bad_backward_tensors(case):
     with pytest.raises(ValueError):
         csa._bwd_args(q, k, v, o, dout, lse, g["dq"], g["dk"], g["dv"],
                       torch.empty(64, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("case", ["ok", "dtype", "shape", "heads axis", "strided"])
+def test_binding_checks_segment_ids(case):
+    q, _, _ = _qkv(shape=(2, 3, 5, 64))
+    B, _, N, _ = q.shape
+    seg = {"ok": torch.zeros(B, N, dtype=torch.int32),
+           "dtype": torch.zeros(B, N, dtype=torch.int64),
+           "shape": torch.zeros(B, N + 1, dtype=torch.int32),
+           "heads axis": torch.zeros(B, 2, N, dtype=torch.int32),
+           "strided": torch.zeros(N, B, dtype=torch.int32).t()}[case]
+    if case == "ok":
+        csa._check_seg(seg, q)
+    else:
+        with pytest.raises(ValueError, match="seg"):
+            csa._check_seg(seg, q)
 
 
 @pytest.mark.parametrize("loss", [torch.empty(1, dtype=torch.float32), torch.empty(2, dtype=torch.float64),
