@@ -245,7 +245,8 @@ __device__ __forceinline__ void dkdv_step(const QStageT<SEG>& sa, int ra, const 
 // masked body too.
 // Without it the predicate is causal (causal = 1) or absent (causal = 0).
 // SEG: only pairs of equal segment ids (seg, [B][N], batch = head / hpb)
-// exist; every stage takes the masked body.
+// exist; the walk covers only the queries whose ids fall in the block's key-id
+// range, and every stage takes the masked body.
 template <bool BANDED, bool SEG>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -291,14 +292,22 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
     }
 
   // queries that see these keys: from the block's first key (causal) or 0, to
-  // the last key's window end or N
-  const int qstart = causal ? kb * kBlk : 0;
-  const int qend = band ? min(N, kb * kBlk + kBlk - 1 + band) : N;
+  // the last key's window end or N (with segment ids, within their span)
+  int qstart = causal ? kb * kBlk : 0;
+  int qend = band ? min(N, kb * kBlk + kBlk - 1 + band) : N;
+  const int32_t* segrow = SEG ? seg + (size_t)(head / hpb) * N : nullptr;
+  if (SEG) {
+    __shared__ int32_t red[2][kWaves][2];
+    int first, last;
+    seg_span<kThreads>(segrow, N, kb * kBlk, kBlk, qstart, qend, tid, red, first, last);
+    // every key is also a query with its own id, so the span is never empty
+    qstart = __builtin_amdgcn_readfirstlane(first);
+    qend = __builtin_amdgcn_readfirstlane(last);
+  }
   const int nst = (qend - qstart + kT2 - 1) / kT2;  // stages of 64 queries
   const uint32_t tbytes = (uint32_t)N * kD * 2, rbytes = (uint32_t)N * 4;
   const __amdgpu_buffer_rsrc_t rq = head_rsrc(q + base, tbytes), ro = head_rsrc(dout + base, tbytes);
   const __amdgpu_buffer_rsrc_t rl = head_rsrc(nlseg + rbase, rbytes), rd = head_rsrc(ndeltag + rbase, rbytes);
-  const int32_t* segrow = SEG ? seg + (size_t)(head / hpb) * N : nullptr;
   __amdgpu_buffer_rsrc_t rs = rl;
   if (SEG) rs = head_rsrc(segrow, rbytes);
   const int32_t sk = SEG && kw + i32 < N ? segrow[kw + i32] : 0;  // the lane's key id

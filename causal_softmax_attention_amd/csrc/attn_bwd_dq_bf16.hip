@@ -207,9 +207,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
     for (int b = 0; b < kQT; ++b) dqacc[a][b] = floatx16{};
 
   // keys of the workgroup's queries: stages t0 .. ntiles-1 of kT2 keys
-  const int t0 = band ? max(0, qb * kBlk - band + 1) / kT2 : 0;
+  int t0 = band ? max(0, qb * kBlk - band + 1) / kT2 : 0;
   const int kend = causal ? min(N, qb * kBlk + kBlk) : N;
-  const int ntiles = (kend + kT2 - 1) / kT2;
+  int ntiles = (kend + kT2 - 1) / kT2;
+  if (SEG) {
+    // only the key tiles within the span of keys whose ids fall in the
+    // block's query-id range (never empty: each query is also a key)
+    __shared__ int32_t red[2][kWaves][2];
+    int first, last;
+    seg_span<kThreads>(segrow, N, qb * kBlk, kBlk, t0 * kT2, kend, threadIdx.x, red, first, last);
+    t0 = __builtin_amdgcn_readfirstlane(first / kT2);
+    ntiles = __builtin_amdgcn_readfirstlane((last + kT2 - 1) / kT2);
+  }
   const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
   const uint32_t tbytes = (uint32_t)N * kD * 2;
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);

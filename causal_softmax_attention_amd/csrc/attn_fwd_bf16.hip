@@ -259,9 +259,9 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
   const int qw = qb * kBr + wave * kQW;              // first query of this wave
   const int wq_last = min(qw + kQW, N) - 1;          // last valid query of the wave
   // keys the workgroup needs: tiles t0 .. ntiles-1
-  const int t0 = band ? max(0, qb * kBr - band + 1) / kBc : 0;
+  int t0 = band ? max(0, qb * kBr - band + 1) / kBc : 0;
   const int kend = causal ? min(N, qb * kBr + kBr) : N;
-  const int ntiles = (kend + kBc - 1) / kBc;
+  int ntiles = (kend + kBc - 1) / kBc;
   const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
 
   // Q operand: lane holds q[qw + 32 qt + i32][16 kk + 8 h .. +7]
@@ -297,6 +297,13 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
     }
     sqlo = __builtin_amdgcn_readfirstlane(sqlo);
     sqhi = __builtin_amdgcn_readfirstlane(sqhi);
+    // only the key tiles within the span of keys whose ids fall in the
+    // block's query-id range (never empty: each query is also a key)
+    __shared__ int32_t red[2][kWaves][2];
+    int first, last;
+    seg_span<kThreads>(segrow, N, qb * kBr, kBr, t0 * kBc, kend, tid, red, first, last);
+    t0 = __builtin_amdgcn_readfirstlane(first / kBc);
+    ntiles = __builtin_amdgcn_readfirstlane((last + kBc - 1) / kBc);
   }
   // reference exponents start finite, so a tile whose pairs are all absent for
   // a lane gives it weights exp2(-inf) = 0, and its first present pair takes the

@@ -39,4 +39,75 @@ template <typename A> __device__ __forceinline__ A neg_inf();
 template <> __device__ __forceinline__ double neg_inf<double>() { return -__builtin_inf(); }
 template <> __device__ __forceinline__ float neg_inf<float>() { return -__builtin_inff(); }
 
+// Segment ids (one int32 per token): the tokens of [qs, qe) that can pair
+// with the tokens [k0, k0 + nk) are those whose id lies in the id range
+// [lo, hi] of the latter.  Sets (first, last) to the first and one past the
+// last such token (first = INT32_MAX, last = 0 if there is none); a token
+// outside that span pairs with none of [k0, k0 + nk).  Workgroup-wide: every
+// thread of the kThreads calls it; red is LDS for 2 x (kThreads / 64) x 2 ints.
+template <int kThreads>
+__device__ __forceinline__ void seg_span(const int32_t* segrow, int N, int k0, int nk, int qs,
+                                         int qe, int tid, int32_t (*red)[kThreads / 64][2],
+                                         int& first, int& last) {
+  constexpr int kW = kThreads / 64;
+  const int lane = tid & 63, wave = tid >> 6;
+  int32_t lo = INT32_MAX, hi = INT32_MIN;
+  for (int j = k0 + tid; j < min(k0 + nk, N); j += kThreads) {
+    const int32_t id = segrow[j];
+    lo = min(lo, id);
+    hi = max(hi, id);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, __shfl_xor(lo, o));
+    hi = max(hi, __shfl_xor(hi, o));
+  }
+  if (lane == 0) {
+    red[0][wave][0] = lo;
+    red[0][wave][1] = hi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    lo = min(lo, red[0][w][0]);
+    hi = max(hi, red[0][w][1]);
+  }
+  // 16 ids per thread per pass, all loads issued before any compare
+  constexpr int kPer = 16;
+  int f = INT32_MAX, l = -1;
+  for (int b = qs; b < qe; b += kPer * kThreads) {
+    int32_t ids[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = b + e * kThreads + tid;
+      ids[e] = i < qe ? segrow[i] : 0;
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const int i = b + e * kThreads + tid;
+      if (i < qe && ids[e] >= lo && ids[e] <= hi) {
+        f = min(f, i);
+        l = max(l, i);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    f = min(f, __shfl_xor(f, o));
+    l = max(l, __shfl_xor(l, o));
+  }
+  if (lane == 0) {
+    red[1][wave][0] = f;
+    red[1][wave][1] = l;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    f = min(f, red[1][w][0]);
+    l = max(l, red[1][w][1]);
+  }
+  first = f;
+  last = l + 1;
+}
+
 }  // namespace attn
