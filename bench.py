@@ -15,9 +15,10 @@ dS^T Q, dS K), 14 D = 896 flops per pair in all.
 roofline: the kernel with the largest share of the step, timed live with HIP
 events on the library's stream (the timer hook of the C ABI), against the
 bf16 dense MFMA peak of MI355X (2516.6 TFLOP/s).  traffic: HBM bytes per
-launch from rocprofv3 FETCH_SIZE/WRITE_SIZE counters recorded in
-profiles/traffic.json, reported only while the kernel's source is unchanged
-since they were taken.
+launch from rocprofv3's L2-to-memory request counters by size class
+(32 RDREQ_32B + 64 RDREQ_64B + 128 RDREQ_128B read, 32 (WRREQ - WRREQ_64B)
++ 64 WRREQ_64B written) recorded in profiles/traffic.json, reported only
+while the kernel's source is unchanged since they were taken.
 
 cpu_baseline: the float64 oracle (test infrastructure, never tuned) on a
 bounded sample of whole heads of the same workload.
@@ -67,10 +68,10 @@ def source_sha(files) -> str:
 
 
 def traffic_for(slot: str):
-    """HBM bytes per launch of `slot` from profiles/traffic.json: rocprofv3
-    FETCH_SIZE + WRITE_SIZE of that kernel, each scaled by the byte count of
-    a plain copy over what the same counter read for it.  None unless the
-    kernel's sources still hash as they did when the counters were taken."""
+    """HBM bytes per launch of `slot` from profiles/traffic.json: the
+    kernel's L2-to-memory read and write requests, each weighted by its size
+    class (a plain 256 MiB copy checks the sums).  None unless the kernel's
+    sources still hash as they did when the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -179,6 +180,22 @@ def time_attention(q, k, v, steps, warmup, with_bwd=True, per_kernel=True, mask=
         for s in slots:
             per[csa.TIMER_NAMES[s]] = sum(e[s][0].elapsed_time(e[s][1]) for e in events) / steps
     return ms, wall, per, (o, lse), per_step
+
+
+def time_alternating(q, k, v, variants, rounds, steps):
+    """Time several step variants (name -> time_attention keywords) in
+    alternating rounds of `steps` steps each, so that clock and temperature
+    drift reach every variant alike.  Returns {name: (median ms over rounds,
+    per-kernel ms of the last round)}."""
+    import statistics
+    got = {name: [] for name in variants}
+    per_last = {}
+    for _ in range(rounds):
+        for name, kw in variants.items():
+            ms, _, per, _, _ = time_attention(q, k, v, steps, 1, **kw)
+            got[name].append(ms)
+            per_last[name] = per
+    return {name: (statistics.median(v_), per_last[name]) for name, v_ in got.items()}
 
 
 def _blas_vendor() -> str:
@@ -325,12 +342,18 @@ def secondary(steps):
                                "kernels_ms": per}
     del q, k, v
     # the same step with the loss fused into the forward (attn_fwd_train +
-    # attn_bwd_from_fwd): the backward's per-row pass is folded away
+    # attn_bwd_from_fwd): the backward's per-row pass is folded away.  Timed in
+    # alternating rounds with the unfused step, so both see the same clock.
     a, (q, k, v), _ = make_inputs("bf16_4k")
-    ms, _, per, _, _ = time_attention(q, k, v, steps, 2, fused=True)
+    alt = time_alternating(q, k, v, {"unfused": {}, "fused": {"fused": True}}, 6,
+                           max(3, steps // 2))
+    ms, per = alt["fused"]
     fl = 14 * D * pairs(256, 4096)
     out["bf16_4k_train_step_fused_loss"] = {"ms": ms, "TFLOP/s": fl / ms / 1e9,
                                             "frac_of_bf16_peak": fl / ms / 1e9 / BF16_PEAK,
+                                            "unfused_ms_same_rounds": alt["unfused"][0],
+                                            "fused_over_unfused": ms / alt["unfused"][0],
+                                            "timing": "medians over 6 alternating rounds",
                                             "kernels_ms": per}
     del q, k, v
     # the other join predicates on the same 8 x 32 x 4096 bf16 inputs; flops
@@ -462,7 +485,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
@@ -470,8 +493,8 @@ def main():
                     help="time only the Q/K/V projection and the long-table adapter (one JSON "
                          "line of those); for profiling their kernels")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="first run a plain 256 MiB device copy (3x), the known-size reference "
-                         "for rocprofv3 FETCH_SIZE / WRITE_SIZE")
+                    help="first run a plain 256 MiB device copy (3x), the known-size check "
+                         "of the byte counts derived from rocprofv3 request counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this library has no multi-GPU path); "
