@@ -309,11 +309,17 @@ class SclkSampler:
             self._thread.join()
 
     def summary(self):
+        # The driver refreshes these readings only every few hundred ms, so the
+        # first readings of a window can still show the idle clock from
+        # before the load: statistics are taken from the first reading that
+        # differs from the window's first one (all readings if none does).
         def stats(v):
             if not v:
                 return None
-            v = sorted(v)
-            return {"median": v[len(v) // 2], "min": v[0], "max": v[-1], "samples": len(v)}
+            first_change = next((i for i, x in enumerate(v) if x != v[0]), 0)
+            w = sorted(v[first_change:])
+            return {"median": w[len(w) // 2], "min": w[0], "max": w[-1], "samples": len(w),
+                    "stale_leading_samples": first_change, "leading_value": v[0]}
         return {"gfx_clock_info_mhz": stats(self.samples),
                 "gpu_metrics_current_gfxclks_mean_mhz": stats(self.xcd_samples),
                 "raw_first_reading": self.raw, "error": self.error}
@@ -524,8 +530,8 @@ def main():
     log(f"timing {args.steps} steps after {args.warmup} warmup")
     ms, wall, per, _, per_step = time_attention(q, k, v, args.steps, args.warmup)
     # the GPU's clock readings refresh more slowly than the ~55 ms timed region,
-    # so the clock is sampled over about a second of the same step right after it
-    sustain = max(50, int(1000.0 / ms))
+    # so the clock is sampled over about 2.5 s of the same step right after it
+    sustain = max(50, int(2500.0 / ms))
     log(f"sampling the graphics clock over {sustain} more steps")
     with SclkSampler(period_s=0.01) as clk:
         sus_ms = time_attention(q, k, v, sustain, 0, per_kernel=False)[0]
