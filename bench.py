@@ -462,7 +462,8 @@ def steps_before_the_path(steps):
     ts, ds, xs = t[p], d[p], x[p]
     del p
     mat = torch.empty_like(md)
-    ws = torch.empty(csa.attn_table_workspace_bytes(T_, D2), dtype=torch.uint8, device=dev)
+    ws = torch.empty(csa.attn_table_workspace_bytes(csa.ATTN_BF16, T_, D2), dtype=torch.uint8,
+                     device=dev)
     st = torch.empty(1, dtype=torch.int32, device=dev)
     ms = _mean_ms(lambda: csa.attn_table_to_matrix(ts, ds, xs, T_, D2, m=mat, workspace=ws,
                                                    status=st, check=False), steps)

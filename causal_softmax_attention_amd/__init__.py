@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
         L.nw_gauss_average.restype = ctypes.c_int
         L.attn_matrix_to_table.argtypes = [ctypes.c_int, i64, i64, vp, vp, vp, vp, vp]
         L.attn_matrix_to_table.restype = ctypes.c_int
-        L.attn_table_workspace_bytes.argtypes = [i64, i64]
+        L.attn_table_workspace_bytes.argtypes = [ctypes.c_int, i64, i64]
         L.attn_table_workspace_bytes.restype = sz
         L.attn_table_to_matrix.argtypes = [ctypes.c_int, i64, vp, vp, vp, i64, i64, vp, vp, vp,
                                            sz, vp]
@@ -397,8 +397,8 @@ def attn_matrix_to_table(m, t=None, d=None, x=None, stream=None):
     return t, d, x
 
 
-def attn_table_workspace_bytes(T: int, D: int) -> int:
-    return lib().attn_table_workspace_bytes(T, D)
+def attn_table_workspace_bytes(dtype_code: int, T: int, D: int) -> int:
+    return lib().attn_table_workspace_bytes(dtype_code, T, D)
 
 
 def attn_table_to_matrix(t, d, x, T: int, D: int, m=None, workspace=None, status=None,
@@ -421,7 +421,7 @@ def attn_table_to_matrix(t, d, x, T: int, D: int, m=None, workspace=None, status
     if (tuple(m.shape) != (T, D) or m.dtype != x.dtype or m.device != x.device
             or not m.is_contiguous()):
         raise ValueError("m must be a contiguous [T, D] tensor of x's dtype on x's device")
-    need = attn_table_workspace_bytes(T, D)
+    need = attn_table_workspace_bytes(_dtype_code(x), T, D)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
     _check_buffer(workspace, x)

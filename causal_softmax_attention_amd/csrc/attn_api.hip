@@ -398,9 +398,16 @@ int nw_gauss_average(int64_t n_targets, const float* tx, const float* ty, int64_
   return hip_status(e, "nw_gauss_average launch");
 }
 
-size_t attn_table_workspace_bytes(int64_t T, int64_t D) {
-  if (T < 1 || D < 1 || T > kMaxCells / D) return 0;
-  return attn::table_workspace_bytes(T, D);
+size_t attn_table_workspace_bytes(attn_dtype_t dtype, int64_t T, int64_t D) {
+  if (dtype != ATTN_F64 && dtype != ATTN_F32 && dtype != ATTN_BF16) {
+    fail(ATTN_EINVAL, "unknown dtype %d", dtype);
+    return 0;
+  }
+  if (T < 1 || D < 1 || T > kMaxCells / D) {
+    fail(ATTN_EINVAL, "T and D must be >= 1 with at most %lld cells", (long long)kMaxCells);
+    return 0;
+  }
+  return attn::table_workspace_bytes((int)elem_size(dtype), T, D);
 }
 
 int attn_table_to_matrix(attn_dtype_t dtype, int64_t rows, const int64_t* t, const int64_t* d,
@@ -417,7 +424,7 @@ int attn_table_to_matrix(attn_dtype_t dtype, int64_t rows, const int64_t* t, con
   if (((uintptr_t)t & 7u) || ((uintptr_t)d & 7u) || ((uintptr_t)x & (es - 1)) ||
       ((uintptr_t)status & 3u) || !aligned16(m) || !aligned16(workspace))
     return fail(ATTN_EINVAL, "misaligned pointer (t, d: 8; x: element; m, workspace: 16; status: 4)");
-  const size_t need = attn::table_workspace_bytes(T, D);
+  const size_t need = attn::table_workspace_bytes((int)es, T, D);
   if (workspace_bytes < need)
     return fail(ATTN_EINVAL, "workspace of %zu bytes is smaller than the %zu required",
                 workspace_bytes, need);

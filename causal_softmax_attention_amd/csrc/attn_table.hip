@@ -6,12 +6,27 @@
 //
 // matrix -> rows: row r = t D + d is (t, d, m[t][d]), in (t, d) order (the
 //   order of the forward's ORDER BY t, d).  One streaming pass.
-// rows -> matrix: every cell starts as NaN (a cell no row names stays NaN, as
-//   a pivot fills holes), then each row writes its cell.  A bitmap in the
-//   caller's workspace (one bit per cell, set with atomicOr) catches a cell
-//   named twice; a coordinate outside [0, T) x [0, D) is skipped.  Both set bits of a status word in device
-//   memory (1: out of range, 2: named twice) that the caller reads after
-//   synchronising; the matrix is unspecified when the status is not 0.
+// rows -> matrix: a cell no row names is NaN (a pivot fills holes), each row
+//   gives its cell its x, a coordinate outside [0, T) x [0, D) is skipped, and
+//   a cell named twice is an error.  Three passes and no per-row atomics
+//   (scattered device atomics run at about a quarter of the rate of scattered
+//   plain stores on this part):
+//     1. clear a staging array in the caller's workspace (one word per cell:
+//        the value's bits and a mark) and two counters;
+//     2. each row stores its value, marked, into its cell's staging word (one
+//        plain store, scattered unless the rows come in cell order) and counts
+//        itself;
+//     3. each cell takes its staged value, or NaN where unmarked, and the marked
+//        cells are counted.
+//   Two rows naming one cell leave one marked word for two counted rows, so
+//   "some cell named twice" is exactly "marked cells < counted rows".
+//   A first pass takes the common case whole: when there are T x D rows and
+//   row r names cell r (the order of ORDER BY t, d), the matrix is a copy of
+//   x.  That pass copies while it checks, and a workgroup stops as soon as any
+//   row breaks the order; the three passes above then run only if one did
+//   (each reads the flag and returns at once otherwise).  Status
+//   bits in a device word (1: out of range, 2: named twice) are read by the
+//   caller after synchronising; the matrix is unspecified when it is not 0.
 //
 // Values are moved as raw bits (2, 4 or 8 bytes), so the pivot is bit-exact
 // for every element type.
@@ -22,83 +37,161 @@ namespace attn {
 namespace {
 
 constexpr int kThr = 256;
+constexpr size_t kCounterBytes = 256;  // workspace head: two counters, then the order flag
 
-// Fill the matrix with the NaN pattern and the bitmap (`words` 32-bit words)
-// with 0, 16 bytes per store; thread 0 clears the status word.
-template <typename U>
-__global__ __launch_bounds__(kThr) void pivot_fill(U* __restrict__ out, uint32_t* __restrict__ seen,
-                                                   int64_t cells, int64_t words, U nan_bits,
-                                                   int32_t* __restrict__ status) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
-  constexpr int kPer = 16 / sizeof(U);
-  U pat[kPer];
+// A cell's staging word: the value's bits and the mark of a row that named it.
+template <typename U> struct StageOf;
+template <> struct StageOf<uint16_t> {  // value | 1 << 16
+  using type = uint32_t;
+  __device__ static uint32_t make(uint16_t v) { return (uint32_t)v | 0x10000u; }
+  __device__ static bool named(uint32_t s) { return (s >> 16) != 0; }
+  __device__ static uint16_t value(uint32_t s) { return (uint16_t)(s & 0xffffu); }
+};
+template <> struct StageOf<uint32_t> {  // {value, 1}
+  using type = uint2;
+  __device__ static uint2 make(uint32_t v) { return make_uint2(v, 1u); }
+  __device__ static bool named(uint2 s) { return s.y != 0; }
+  __device__ static uint32_t value(uint2 s) { return s.x; }
+};
+template <> struct StageOf<uint64_t> {  // {low, high, 1, 0}
+  using type = uint4;
+  __device__ static uint4 make(uint64_t v) {
+    return make_uint4((uint32_t)v, (uint32_t)(v >> 32), 1u, 0u);
+  }
+  __device__ static bool named(uint4 s) { return s.z != 0; }
+  __device__ static uint64_t value(uint4 s) { return (uint64_t)s.x | ((uint64_t)s.y << 32); }
+};
+
+// Sum of one unsigned long long per thread over the workgroup, added to *dst
+// by thread 0 (one device atomic per workgroup).
+__device__ __forceinline__ void block_add(unsigned long long v, unsigned long long* dst) {
+  __shared__ unsigned long long part[kThr / 64];
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) pat[e] = nan_bits;
-  const uint4 nan16 = *(const uint4*)pat;
-  const int64_t stride = (int64_t)gridDim.x * kThr;
-  const int64_t vec = cells / kPer;
-  for (int64_t i = (int64_t)blockIdx.x * kThr + threadIdx.x; i < vec; i += stride)
-    ((uint4*)out)[i] = nan16;
-  for (int64_t i = vec * kPer + (int64_t)blockIdx.x * kThr + threadIdx.x; i < cells; i += stride)
-    out[i] = nan_bits;
-  const int64_t wvec = words / 4;
-  for (int64_t i = (int64_t)blockIdx.x * kThr + threadIdx.x; i < wvec; i += stride)
-    ((uint4*)seen)[i] = make_uint4(0, 0, 0, 0);
-  for (int64_t i = wvec * 4 + (int64_t)blockIdx.x * kThr + threadIdx.x; i < words; i += stride)
-    seen[i] = 0;
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned long long s = 0;
+#pragma unroll
+    for (int w = 0; w < kThr / 64; ++w) s += part[w];
+    if (s) atomicAdd(dst, s);
+  }
 }
 
-// Each row writes its cell; the cell's bit, already set, tells a second write.
-// A wave whose 64 rows name 64 consecutive cells (rows in (t, d) order, as the
-// forward's ORDER BY returns them) sets the bits of that run with one atomicOr
-// per 32-bit word it covers (at most three) instead of 64 on the same words.
+// Set-up: clear the counters and the status word; the order flag starts set
+// unless there are exactly T x D rows.
+__global__ void pivot_init(unsigned long long* __restrict__ counters, uint32_t* __restrict__ broken,
+                           int32_t* __restrict__ status, int64_t rows, int64_t cells) {
+  if (threadIdx.x == 0) {
+    counters[0] = 0;
+    counters[1] = 0;
+    *broken = rows != cells;
+    *status = 0;
+  }
+}
+
+// The ordered pass: row r names cell r (and lies in range) -> copy its value;
+// any other row sets the flag, and every workgroup returns once it sees the
+// flag set.  (Element-sized accesses: t, d and x need only their natural
+// alignment.)
 template <typename U>
-__global__ __launch_bounds__(kThr) void pivot_scatter(const int64_t* __restrict__ t,
+__global__ __launch_bounds__(kThr) void pivot_ordered(const int64_t* __restrict__ t,
                                                       const int64_t* __restrict__ d,
                                                       const U* __restrict__ x, int64_t rows,
                                                       int64_t T, int64_t D, U* __restrict__ out,
-                                                      uint32_t* __restrict__ seen,
-                                                      int32_t* __restrict__ status) {
-  int flags = 0;
-  const int lane = threadIdx.x & 63;
+                                                      uint32_t* __restrict__ broken) {
   const int64_t stride = (int64_t)gridDim.x * kThr;
-  const int64_t first = (int64_t)blockIdx.x * kThr + (threadIdx.x & ~63);  // the wave's first row
-  for (int64_t r0 = first; r0 < rows; r0 += stride) {
-    const int64_t r = r0 + lane;
-    const bool live = r < rows;
-    int64_t cell = -1;
-    bool ok = false;
-    if (live) {
-      const int64_t ti = t[r], di = d[r];
-      ok = ti >= 0 && ti < T && di >= 0 && di < D;
-      if (!ok) flags |= 1;
-      cell = ok ? ti * D + di : -1;
-    }
-    // a run of 64 consecutive cells across the wave (all rows live and in range)
-    const int64_t c0 = __shfl(cell, 0);
-    const bool run = __all(live && ok && cell == c0 + lane);
-    if (run) {
-      // bits [c0, c0 + 64) span words w0 .. w0 + 2; lane k < 3 owns word w0 + k
-      const int64_t w0 = c0 >> 5;
-      const int sh = (int)(c0 & 31);
-      if (lane < 3) {
-        // bits of word w0 + lane covered by the run [sh, sh + 64) (relative to w0)
-        const int lo = 32 * lane, hi = lo + 32;
-        const int a = sh > lo ? sh : lo, b = sh + 64 < hi ? sh + 64 : hi;
-        if (a < b) {
-          const uint32_t mask = (b - a == 32 ? 0xffffffffu : ((1u << (b - a)) - 1u)) << (a - lo);
-          if (atomicOr(seen + w0 + lane, mask) & mask) flags |= 2;
-        }
-      }
-    } else if (live && ok) {
-      const uint32_t bit = 1u << (cell & 31);
-      if (atomicOr(seen + (cell >> 5), bit) & bit) flags |= 2;
-    }
-    if (live && ok) out[cell] = x[r];
+  for (int64_t r = (int64_t)blockIdx.x * kThr + threadIdx.x; r < rows; r += stride) {
+    if (*(volatile uint32_t*)broken) return;
+    const int64_t ti = t[r], di = d[r];
+    if (ti >= 0 && ti < T && di >= 0 && di < D && ti * D + di == r) out[r] = x[r];
+    else *broken = 1;
   }
-  // one status update per wave
-  const int any1 = __any(flags & 1), any2 = __any(flags & 2);
-  if (lane == 0 && (any1 | any2)) atomicOr(status, (any1 ? 1 : 0) | (any2 ? 2 : 0));
+}
+
+// Pass 1: zero `words` 32-bit words of staging (16 bytes per store where it
+// can).
+__global__ __launch_bounds__(kThr) void pivot_clear(uint32_t* __restrict__ stage, int64_t words,
+                                                    const uint32_t* __restrict__ broken) {
+  if (!*broken) return;
+  const int64_t stride = (int64_t)gridDim.x * kThr;
+  const int64_t vec = words / 4;
+  for (int64_t i = (int64_t)blockIdx.x * kThr + threadIdx.x; i < vec; i += stride)
+    ((uint4*)stage)[i] = make_uint4(0, 0, 0, 0);
+  for (int64_t i = vec * 4 + (int64_t)blockIdx.x * kThr + threadIdx.x; i < words; i += stride)
+    stage[i] = 0;
+}
+
+// Pass 2: each row in range stores its marked value into its cell's staging
+// word and counts itself (counters[0]); a row out of range sets status bit 1.
+template <typename U>
+__global__ __launch_bounds__(kThr) void pivot_stage(const int64_t* __restrict__ t,
+                                                    const int64_t* __restrict__ d,
+                                                    const U* __restrict__ x, int64_t rows,
+                                                    int64_t T, int64_t D,
+                                                    typename StageOf<U>::type* __restrict__ stage,
+                                                    unsigned long long* __restrict__ counters,
+                                                    int32_t* __restrict__ status,
+                                                    const uint32_t* __restrict__ broken) {
+  if (!*broken) return;
+  using S = StageOf<U>;
+  unsigned long long named = 0;
+  int bad = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThr;
+  for (int64_t r = (int64_t)blockIdx.x * kThr + threadIdx.x; r < rows; r += stride) {
+    const int64_t ti = t[r], di = d[r];
+    if (ti >= 0 && ti < T && di >= 0 && di < D) {
+      stage[ti * D + di] = S::make(x[r]);
+      ++named;
+    } else {
+      bad = 1;
+    }
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(status, 1);
+  block_add(named, counters);
+}
+
+// Pass 3: each cell takes its staged value, or the NaN pattern where no row
+// named it; the named cells are counted (counters[1]).  kPer cells per step
+// (16 bytes of staging words).
+template <typename U>
+__global__ __launch_bounds__(kThr) void pivot_emit(const typename StageOf<U>::type* __restrict__ stage,
+                                                   int64_t cells, U* __restrict__ out, U nan_bits,
+                                                   unsigned long long* __restrict__ counters,
+                                                   const uint32_t* __restrict__ broken) {
+  if (!*broken) return;
+  using S = StageOf<U>;
+  using W = typename S::type;
+  constexpr int kPer = 16 / sizeof(W);
+  unsigned long long named = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThr;
+  const int64_t groups = cells / kPer;
+  for (int64_t g = (int64_t)blockIdx.x * kThr + threadIdx.x; g < groups; g += stride) {
+    W w[kPer];
+    *(uint4*)w = ((const uint4*)stage)[g];
+    U v[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const bool n = S::named(w[e]);
+      named += n;
+      v[e] = n ? S::value(w[e]) : nan_bits;
+    }
+    static_assert(kPer * sizeof(U) == 8, "a group is 8 bytes of output");
+    *(uint2*)(out + g * kPer) = *(const uint2*)v;
+  }
+  for (int64_t c = groups * kPer + (int64_t)blockIdx.x * kThr + threadIdx.x; c < cells; c += stride) {
+    const W w = stage[c];
+    const bool n = S::named(w);
+    named += n;
+    out[c] = n ? S::value(w) : nan_bits;
+  }
+  block_add(named, counters + 1);
+}
+
+// Fewer marked cells than rows in range: some cell was named twice.
+__global__ void pivot_check(const unsigned long long* __restrict__ counters,
+                            int32_t* __restrict__ status) {
+  if (threadIdx.x == 0 && counters[1] != counters[0]) atomicOr(status, 2);
 }
 
 // Rows (t, d, x) of a T x D matrix in (t, d) order.  A thread handles pairs of
@@ -144,19 +237,32 @@ unsigned grid_for(int64_t n) {
   return (unsigned)(b < 1 ? 1 : b > 8192 ? 8192 : b);
 }
 
-int64_t bitmap_words(int64_t cells) { return (cells + 31) / 32; }
+size_t stage_bytes(int elem_bytes) { return elem_bytes == 8 ? 16 : elem_bytes == 4 ? 8 : 4; }
 
 template <typename U>
 hipError_t pivot(int64_t rows, const int64_t* t, const int64_t* d, const void* x, int64_t T,
                  int64_t D, void* out, int32_t* status, void* workspace, U nan_bits,
                  hipStream_t stream, const Timers& tm) {
+  using W = typename StageOf<U>::type;
   const int64_t cells = T * D;
-  uint32_t* seen = (uint32_t*)workspace;
-  hipLaunchKernelGGL(pivot_fill<U>, dim3(grid_for(cells / 8 + 1)), dim3(kThr), 0, stream, (U*)out,
-                     seen, cells, bitmap_words(cells), nan_bits, status);
+  unsigned long long* counters = (unsigned long long*)workspace;
+  uint32_t* broken = (uint32_t*)(counters + 2);
+  W* stage = (W*)((char*)workspace + kCounterBytes);
+  const int64_t words = cells * (int64_t)(sizeof(W) / 4);
   if (hipError_t e = mark(tm.start[kTimerTable], stream)) return e;
-  hipLaunchKernelGGL(pivot_scatter<U>, dim3(grid_for(rows)), dim3(kThr), 0, stream, t, d,
-                     (const U*)x, rows, T, D, (U*)out, seen, status);
+  hipLaunchKernelGGL(pivot_init, dim3(1), dim3(64), 0, stream, counters, broken, status, rows,
+                     cells);
+  hipLaunchKernelGGL(pivot_ordered<U>, dim3(grid_for(rows)), dim3(kThr), 0, stream, t, d,
+                     (const U*)x, rows, T, D, (U*)out, broken);
+  hipLaunchKernelGGL(pivot_clear, dim3(grid_for(words / 4 + 1)), dim3(kThr), 0, stream,
+                     (uint32_t*)stage, words, (const uint32_t*)broken);
+  hipLaunchKernelGGL(pivot_stage<U>, dim3(grid_for(rows)), dim3(kThr), 0, stream, t, d,
+                     (const U*)x, rows, T, D, stage, counters, status, (const uint32_t*)broken);
+  hipLaunchKernelGGL(pivot_emit<U>, dim3(grid_for(cells / (16 / sizeof(W)) + 1)), dim3(kThr), 0,
+                     stream, (const W*)stage, cells, (U*)out, nan_bits, counters,
+                     (const uint32_t*)broken);
+  hipLaunchKernelGGL(pivot_check, dim3(1), dim3(64), 0, stream, (const unsigned long long*)counters,
+                     status);
   if (hipError_t e = mark(tm.stop[kTimerTable], stream)) return e;
   return hipGetLastError();
 }
@@ -172,8 +278,9 @@ hipError_t unpivot(int64_t T, int64_t D, const void* m, int64_t* t, int64_t* d, 
 
 }  // namespace
 
-size_t table_workspace_bytes(int64_t T, int64_t D) {
-  return (size_t)((bitmap_words(T * D) + 3) / 4 * 16);  // whole 16-byte stores
+size_t table_workspace_bytes(int elem_bytes, int64_t T, int64_t D) {
+  // the counters, then one staging word per cell, in whole 16-byte stores
+  return kCounterBytes + ((size_t)(T * D) * stage_bytes(elem_bytes) + 15) / 16 * 16;
 }
 
 hipError_t launch_table_to_matrix(int elem_bytes, int64_t rows, const int64_t* t, const int64_t* d,

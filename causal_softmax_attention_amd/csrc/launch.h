@@ -100,7 +100,7 @@ hipError_t launch_nw(int64_t n_targets, const float* tx, const float* ty, int64_
                      hipStream_t stream, const Timers& tm);
 
 // Long-table <-> matrix adapter (attn_table.hip).  elem_bytes: 8, 4 or 2.
-size_t table_workspace_bytes(int64_t T, int64_t D);
+size_t table_workspace_bytes(int elem_bytes, int64_t T, int64_t D);
 hipError_t launch_table_to_matrix(int elem_bytes, int64_t rows, const int64_t* t, const int64_t* d,
                                   const void* x, int64_t T, int64_t D, void* out, int32_t* status,
                                   void* workspace, hipStream_t stream, const Timers& tm);

@@ -232,14 +232,18 @@ ATTN_API int nw_gauss_average(int64_t n_targets, const float* tx, const float* t
  *   neither happened, else the OR of 1 (some coordinate out of range) and 2
  *   (some cell named twice), in which case m is unspecified.  The caller reads
  *   *status after synchronising the stream.  `workspace` holds
- *   attn_table_workspace_bytes(T, D) bytes of scratch (one bit per cell).
+ *   attn_table_workspace_bytes(dtype, T, D) bytes of scratch: 256 bytes, then
+ *   one staging word per cell (4 bytes for ATTN_BF16, 8 for ATTN_F32, 16 for
+ *   ATTN_F64); it needs no initialisation.  The call makes no per-row atomic
+ *   update: a doubly named cell is found by counting.
  *   Alignment: t, d 8 bytes; x one element; m and workspace 16 bytes;
  *   status 4 bytes.  m, the workspace and status must not overlap the inputs
  *   or each other.  At most 2^40 rows and 2^40 cells (ATTN_EINVAL).
- *   attn_table_workspace_bytes returns 0 for sizes the call would reject. */
+ *   attn_table_workspace_bytes returns 0 (and sets attn_last_error()) for a
+ *   dtype or sizes the call would reject. */
 ATTN_API int attn_matrix_to_table(attn_dtype_t dtype, int64_t T, int64_t D, const void* m, int64_t* t,
                                   int64_t* d, void* x, void* stream);
-ATTN_API size_t attn_table_workspace_bytes(int64_t T, int64_t D);
+ATTN_API size_t attn_table_workspace_bytes(attn_dtype_t dtype, int64_t T, int64_t D);
 ATTN_API int attn_table_to_matrix(attn_dtype_t dtype, int64_t rows, const int64_t* t, const int64_t* d,
                                   const void* x, int64_t T, int64_t D, void* m, int32_t* status,
                                   void* workspace, size_t workspace_bytes, void* stream);

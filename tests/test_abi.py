@@ -286,15 +286,21 @@ def test_matrix_to_table_rejects(L):
 
 
 def test_table_workspace_bytes(L):
-    assert L.attn_table_workspace_bytes(4, 8) == 16            # one bit per cell, whole 16 B
-    assert L.attn_table_workspace_bytes(1000, 64) == (1000 * 64 // 32) * 4
-    assert L.attn_table_workspace_bytes(0, 8) == 0
-    assert L.attn_table_workspace_bytes(1 << 30, 1 << 20) == 0
+    # 256 bytes of counters, then a staging word per cell (bf16 4, f32 8, f64 16
+    # bytes) in whole 16-byte stores
+    assert L.attn_table_workspace_bytes(csa.ATTN_BF16, 4, 8) == 256 + 128
+    assert L.attn_table_workspace_bytes(csa.ATTN_BF16, 3, 1) == 256 + 16
+    assert L.attn_table_workspace_bytes(csa.ATTN_F32, 1000, 64) == 256 + 1000 * 64 * 8
+    assert L.attn_table_workspace_bytes(csa.ATTN_F64, 1000, 64) == 256 + 1000 * 64 * 16
+    assert L.attn_table_workspace_bytes(csa.ATTN_BF16, 0, 8) == 0
+    assert L.attn_table_workspace_bytes(csa.ATTN_BF16, 1 << 30, 1 << 20) == 0
+    assert L.attn_table_workspace_bytes(9, 4, 8) == 0
+    assert "dtype" in csa.attn_last_error()
 
 
 def test_table_to_matrix_rejects(L):
     t, d, x, m, st, ws = (_addr(i) for i in range(6))
-    need = L.attn_table_workspace_bytes(4, 8)
+    need = L.attn_table_workspace_bytes(csa.ATTN_F32, 4, 8)
     call = lambda dtype=1, rows=32, t=t, d=d, x=x, T=4, D=8, m=m, st=st, ws=ws, wb=need: \
         L.attn_table_to_matrix(dtype, rows, t, d, x, T, D, m, st, ws, wb, None)
     assert call(dtype=9) == csa.ATTN_EINVAL
@@ -334,7 +340,7 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     with pytest.raises(RuntimeError, match="is missing"):
         csa.lib()
     with pytest.raises(RuntimeError, match="is missing"):
-        csa.attn_table_workspace_bytes(4, 4)
+        csa.attn_table_workspace_bytes(csa.ATTN_BF16, 4, 4)
 
 
 @pytest.mark.parametrize("B,H,N,ok", [

@@ -124,11 +124,58 @@ def test_table_to_matrix_status(case, code):
     assert int(status2.item()) == 0
 
 
+@pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
+def test_complete_tables_near_order(dtype):
+    """T x D rows that are almost in (t, d) order: two rows swapped (a valid
+    table: the pivot equals the oracle's bit for bit), and one row renamed to
+    its neighbour's cell (a cell named twice and a hole: status 2)."""
+    import causal_softmax_attention_amd as csa
+    T, D = 37, 64
+    m = _values(23, T, D, dtype)
+    t, d, x = tables.table(m.view(NP_BITS[dtype]))
+    for i, j in ((0, 1), (1000, 2367), (T * D - 2, T * D - 1)):
+        p = np.arange(T * D)
+        p[i], p[j] = p[j], p[i]
+        note(f"near-ordered swap {i} {j} {dtype}")
+        got = csa.attn_table_to_matrix(torch.from_numpy(t[p]).to(DEV),
+                                       torch.from_numpy(d[p]).to(DEV), _to_dev(x[p], dtype), T, D)
+        torch.cuda.synchronize()
+        src = tables.matrix(t[p], d[p], np.arange(T * D, dtype=np.float64), T, D)
+        assert np.array_equal(_bits(got, dtype).reshape(-1), x[p][src.reshape(-1).astype(np.int64)])
+    for i in (0, 700, T * D - 1):
+        t2, d2 = t.copy(), d.copy()
+        k = i + 1 if i + 1 < T * D else i - 1
+        t2[i], d2[i] = t[k], d[k]
+        note(f"near-ordered duplicate at {i} {dtype}")
+        _, status = csa.attn_table_to_matrix(torch.from_numpy(t2).to(DEV),
+                                             torch.from_numpy(d2).to(DEV), _to_dev(x, dtype), T, D,
+                                             check=False)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 2
+
+
+def test_duplicate_with_equal_values():
+    """The same row (t, d, x) sent twice is still a cell named twice, and a
+    duplicate whose second copy lies out of range is not: it is skipped."""
+    import causal_softmax_attention_amd as csa
+    T, D = 4, 3
+    t, d, x = tables.table(np.arange(T * D, dtype=np.float32).reshape(T, D))
+    for extra_t, code in ((t[5], 2), (T + 1, 1)):
+        t2 = np.concatenate([t, [extra_t]])
+        d2 = np.concatenate([d, d[5:6]])
+        x2 = np.concatenate([x, x[5:6]])
+        note(f"duplicate row, extra t={extra_t}")
+        _, status = csa.attn_table_to_matrix(*(torch.from_numpy(a).to(DEV) for a in (t2, d2, x2)),
+                                             T, D, check=False)
+        torch.cuda.synchronize()
+        assert int(status.item()) == code
+
+
 @pytest.mark.parametrize("where", ["run", "lane"])
 def test_duplicate_in_ordered_rows(where):
-    """An ordered table with one 64-row stretch sent twice: whole waves of
-    consecutive cells see it through the run's word masks ("run": the repeat
-    starts on a wave boundary), other waves through their lanes' bits."""
+    """An ordered table with one 64-row stretch sent twice, starting on a
+    64-row boundary ("run") or off it ("lane"): the repeated rows store into
+    cells already staged, so fewer cells are marked than rows counted."""
     import causal_softmax_attention_amd as csa
     T, D = 8, 64
     t, d, x = tables.table(np.arange(T * D, dtype=np.float32).reshape(T, D))
