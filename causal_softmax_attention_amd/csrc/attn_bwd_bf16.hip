@@ -296,13 +296,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   int qstart = causal ? kb * kBlk : 0;
   int qend = band ? min(N, kb * kBlk + kBlk - 1 + band) : N;
   const int32_t* segrow = SEG ? seg + (size_t)(head / hpb) * N : nullptr;
+  bool seg_uniform = false;  // every query of the walk has the block's one key id
   if (SEG) {
-    __shared__ int32_t red[2][kWaves][2];
-    int first, last;
-    seg_span<kThreads>(segrow, N, kb * kBlk, kBlk, qstart, qend, tid, red, first, last);
+    __shared__ int32_t red[2][kWaves][4];
+    const SegSpan sp = seg_span<kThreads>(segrow, N, kb * kBlk, kBlk, qstart, qend, tid, red);
     // every key is also a query with its own id, so the span is never empty
-    qstart = __builtin_amdgcn_readfirstlane(first);
-    qend = __builtin_amdgcn_readfirstlane(last);
+    qstart = __builtin_amdgcn_readfirstlane(sp.first);
+    qend = __builtin_amdgcn_readfirstlane(sp.last);
+    seg_uniform = sp.lo == sp.hi && sp.dense;
   }
   const int nst = (qend - qstart + kT2 - 1) / kT2;  // stages of 64 queries
   const uint32_t tbytes = (uint32_t)N * kD * 2, rbytes = (uint32_t)N * 4;
@@ -336,12 +337,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16(
   // them: stage s does once its last query minus the block's first key
   // reaches band, i.e. from stage edge on.  Stages 2 .. edge - 1 (rounded down
   // to whole turns of the 3-stage ring) take the plain body, the rest the
-  // masked one.
+  // masked one.  With segment ids the ids mask too, except where every query
+  // of the walk shares the block's single key id: then the stages that lie
+  // wholly inside the walk need only the base predicate.
   static_assert(kBlk == 2 * kT2, "the block's diagonal spans stages 0 and 1");
   using T = std::true_type;
   using Fl = std::false_type;
   const int edge = BANDED ? (band - kT2 + 1 + kb * kBlk - qstart + kT2 - 1) / kT2 : nst;
-  const int plain_end = SEG ? 2 : BANDED ? 2 + 3 * (max(edge - 2, 0) / 3) : nst;
+  const int whole = seg_uniform ? (qend - qstart) / kT2 : 2;  // segments: stages wholly inside
+  const int plain_end = SEG ? 2 + 3 * (max(min(BANDED ? edge : nst, whole) - 2, 0) / 3)
+                            : BANDED ? 2 + 3 * (max(edge - 2, 0) / 3) : nst;
 
   issue(st0, 0);
   if (nst > 1) issue(st1, 1);

@@ -213,11 +213,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
   if (SEG) {
     // only the key tiles within the span of keys whose ids fall in the
     // block's query-id range (never empty: each query is also a key)
-    __shared__ int32_t red[2][kWaves][2];
-    int first, last;
-    seg_span<kThreads>(segrow, N, qb * kBlk, kBlk, t0 * kT2, kend, threadIdx.x, red, first, last);
-    t0 = __builtin_amdgcn_readfirstlane(first / kT2);
-    ntiles = __builtin_amdgcn_readfirstlane((last + kT2 - 1) / kT2);
+    __shared__ int32_t red[2][kWaves][4];
+    const SegSpan sp = seg_span<kThreads>(segrow, N, qb * kBlk, kBlk, t0 * kT2, kend, threadIdx.x, red);
+    t0 = __builtin_amdgcn_readfirstlane(sp.first / kT2);
+    ntiles = __builtin_amdgcn_readfirstlane((sp.last + kT2 - 1) / kT2);
   }
   const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
   const uint32_t tbytes = (uint32_t)N * kD * 2;

@@ -304,11 +304,10 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
     sqhi = __builtin_amdgcn_readfirstlane(sqhi);
     // only the key tiles within the span of keys whose ids fall in the
     // block's query-id range (never empty: each query is also a key)
-    __shared__ int32_t red[2][kWaves][2];
-    int first, last;
-    seg_span<kThreads>(segrow, N, qb * kBr, kBr, t0 * kBc, kend, tid, red, first, last);
-    t0 = __builtin_amdgcn_readfirstlane(first / kBc);
-    ntiles = __builtin_amdgcn_readfirstlane((last + kBc - 1) / kBc);
+    __shared__ int32_t red[2][kWaves][4];
+    const SegSpan sp = seg_span<kThreads>(segrow, N, qb * kBr, kBr, t0 * kBc, kend, tid, red);
+    t0 = __builtin_amdgcn_readfirstlane(sp.first / kBc);
+    ntiles = __builtin_amdgcn_readfirstlane((sp.last + kBc - 1) / kBc);
   }
   // reference exponents start finite, so a tile whose pairs are all absent for
   // a lane gives it weights exp2(-inf) = 0, and its first present pair takes the

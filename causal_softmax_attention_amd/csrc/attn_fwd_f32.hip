@@ -224,11 +224,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_f32_kernel(
   if (SEG) {
     // only the key tiles within the span of keys whose ids fall in the
     // block's query-id range (never empty: each query is also a key)
-    __shared__ int32_t red[2][kWaves][2];
-    int first, last;
-    seg_span<kThreads>(segrow, N, qb * kBr, kBr, t0 * kBc, kend, threadIdx.x, red, first, last);
-    t0 = __builtin_amdgcn_readfirstlane(first / kBc);
-    ntiles = __builtin_amdgcn_readfirstlane((last + kBc - 1) / kBc);
+    __shared__ int32_t red[2][kWaves][4];
+    const SegSpan sp = seg_span<kThreads>(segrow, N, qb * kBr, kBr, t0 * kBc, kend, threadIdx.x, red);
+    t0 = __builtin_amdgcn_readfirstlane(sp.first / kBc);
+    ntiles = __builtin_amdgcn_readfirstlane((sp.last + kBc - 1) / kBc);
   }
   const int wlo = band ? qw - band + 1 : 0, whi = causal ? wq_last : N - 1;  // keys of this wave
   const int qi = qw + i32;

@@ -41,16 +41,31 @@ template <> __device__ __forceinline__ float neg_inf<float>() { return -__builti
 
 // Segment ids (one int32 per token): the tokens of [qs, qe) that can pair
 // with the tokens [k0, k0 + nk) are those whose id lies in the id range
-// [lo, hi] of the latter.  Sets (first, last) to the first and one past the
-// last such token (first = INT32_MAX, last = 0 if there is none); a token
-// outside that span pairs with none of [k0, k0 + nk).  Workgroup-wide: every
-// thread of the kThreads calls it; red is LDS for 2 x (kThreads / 64) x 2 ints.
+// [lo, hi] of the latter.  first / last: the first and one past the last such
+// token (first = INT32_MAX, last = 0 if there is none); a token outside that
+// span pairs with none of [k0, k0 + nk).  dense: every token of the span has
+// its id in [lo, hi].  Workgroup-wide: every thread of the kThreads calls it;
+// red is LDS for 2 x (kThreads / 64) x 4 ints.
+struct SegSpan {
+  int first, last;
+  int32_t lo, hi;
+  bool dense;
+};
+
 template <int kThreads>
-__device__ __forceinline__ void seg_span(const int32_t* segrow, int N, int k0, int nk, int qs,
-                                         int qe, int tid, int32_t (*red)[kThreads / 64][2],
-                                         int& first, int& last) {
+__device__ __forceinline__ SegSpan seg_span(const int32_t* segrow, int N, int k0, int nk, int qs,
+                                            int qe, int tid, int32_t (*red)[kThreads / 64][4]) {
   constexpr int kW = kThreads / 64;
+  constexpr int kPer = 16;  // ids per thread per pass over [qs, qe)
   const int lane = tid & 63, wave = tid >> 6;
+  // the first pass's loads are issued with the block's own ids, so the two
+  // round trips overlap
+  int32_t ids[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const int i = qs + e * kThreads + tid;
+    ids[e] = i < qe ? segrow[i] : 0;
+  }
   int32_t lo = INT32_MAX, hi = INT32_MIN;
   for (int j = k0 + tid; j < min(k0 + nk, N); j += kThreads) {
     const int32_t id = segrow[j];
@@ -72,15 +87,14 @@ __device__ __forceinline__ void seg_span(const int32_t* segrow, int N, int k0, i
     lo = min(lo, red[0][w][0]);
     hi = max(hi, red[0][w][1]);
   }
-  // 16 ids per thread per pass, all loads issued before any compare
-  constexpr int kPer = 16;
-  int f = INT32_MAX, l = -1;
+  int f = INT32_MAX, l = -1, cnt = 0;
   for (int b = qs; b < qe; b += kPer * kThreads) {
-    int32_t ids[kPer];
+    if (b != qs) {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) {
-      const int i = b + e * kThreads + tid;
-      ids[e] = i < qe ? segrow[i] : 0;
+      for (int e = 0; e < kPer; ++e) {
+        const int i = b + e * kThreads + tid;
+        ids[e] = i < qe ? segrow[i] : 0;
+      }
     }
 #pragma unroll
     for (int e = 0; e < kPer; ++e) {
@@ -88,6 +102,7 @@ __device__ __forceinline__ void seg_span(const int32_t* segrow, int N, int k0, i
       if (i < qe && ids[e] >= lo && ids[e] <= hi) {
         f = min(f, i);
         l = max(l, i);
+        ++cnt;
       }
     }
   }
@@ -95,19 +110,22 @@ __device__ __forceinline__ void seg_span(const int32_t* segrow, int N, int k0, i
   for (int o = 32; o >= 1; o >>= 1) {
     f = min(f, __shfl_xor(f, o));
     l = max(l, __shfl_xor(l, o));
+    cnt += __shfl_xor(cnt, o);
   }
   if (lane == 0) {
     red[1][wave][0] = f;
     red[1][wave][1] = l;
+    red[1][wave][2] = cnt;
   }
   __syncthreads();
+  cnt = 0;
 #pragma unroll
   for (int w = 0; w < kW; ++w) {
     f = min(f, red[1][w][0]);
     l = max(l, red[1][w][1]);
+    cnt += red[1][w][2];
   }
-  first = f;
-  last = l + 1;
+  return SegSpan{f, l + 1, lo, hi, cnt == l + 1 - f};
 }
 
 }  // namespace attn

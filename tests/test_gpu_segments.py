@@ -142,6 +142,33 @@ def test_inf_value_within_its_segment(dtype):
         assert_close(f"lse inf {mask}", to_host(lse)[0, 0], wl, TOL[dtype])
 
 
+@pytest.mark.parametrize("pattern", ["long documents", "a document split by another",
+                                     "ids returning", "two long documents, full mask"])
+def test_seg_uniform_blocks(pattern):
+    """bf16 fwd + bwd where whole key blocks lie in one document, so the
+    dK/dV walk takes the plain body on stages wholly inside their document:
+    long contiguous documents; one document interrupted by another (its key
+    blocks see the other document's rows inside their span, which must stay
+    masked); ids that come back after other ids; and the full predicate."""
+    B, H, N = 1, 2, 1500
+    mask = "full" if "full" in pattern else "causal"
+    if pattern == "long documents":
+        seg = np.repeat(np.arange(3), [700, 500, 300])[None]
+    elif pattern == "a document split by another":
+        seg = np.concatenate([np.zeros(600), np.ones(300), np.zeros(600)]).astype(np.int64)[None]
+    elif pattern == "ids returning":
+        seg = np.tile(np.repeat([4, 9], 250), 3)[None]
+    else:
+        seg = np.repeat(np.arange(2), [1000, 500])[None]
+    a = inp.attention_inputs(1234, B, H, N, "bf16")
+    note(f"uniform segment blocks: {pattern}")
+    q, k, v = (to_dev(getattr(a, x), "bf16") for x in "qkv")
+    sd = _seg_dev(seg)
+    o, lse = run_fwd(q, k, v, S, mask=mask, seg=sd)
+    grads = run_bwd(q, k, v, o, o, lse, S, mask=mask, seg=sd)
+    _check(a, seg, o, lse, grads, mask, 0)
+
+
 def _segment_starts_equal_v(o, v, seg, tol):
     """Causal with contiguous documents: a document's first row sees only its
     own key, so o there equals v (any size, every head)."""
