@@ -234,8 +234,10 @@ ATTN_API int nw_gauss_average(int64_t n_targets, const float* tx, const float* t
  *   *status after synchronising the stream.  `workspace` holds
  *   attn_table_workspace_bytes(dtype, T, D) bytes of scratch: 256 bytes, then
  *   one staging word per cell (4 bytes for ATTN_BF16, 8 for ATTN_F32, 16 for
- *   ATTN_F64); it needs no initialisation.  The call makes no per-row atomic
- *   update: a doubly named cell is found by counting.
+ *   ATTN_F64), then for tables of at least 65536 cells about 4 MiB more (the
+ *   counts of a sort of the rows by cell block); it needs no initialisation.
+ *   The call makes no per-row device atomic: a doubly named cell is found by
+ *   counting.
  *   Alignment: t, d 8 bytes; x one element; m and workspace 16 bytes;
  *   status 4 bytes.  m, the workspace and status must not overlap the inputs
  *   or each other.  At most 2^40 rows and 2^40 cells (ATTN_EINVAL).

@@ -196,6 +196,55 @@ def test_duplicate_in_ordered_rows(where):
     assert np.array_equal(got.cpu().numpy(), tables.matrix(t, d, x, T, D))
 
 
+@pytest.mark.parametrize("dtype", ["f64", "f32", "bf16"])
+@pytest.mark.parametrize("T,D,holes", [(300, 301, 0), (300, 301, 1000), (257, 512, 3)])
+def test_table_to_matrix_binned(dtype, T, D, holes):
+    """Tables of at least 65536 shuffled rows and cells take the binned form
+    (rows sorted by cell block, one workgroup per block); the last block is
+    partial when T*D is not a multiple of the block size."""
+    import causal_softmax_attention_amd as csa
+    m = _values(60 + T + D, T, D, dtype)
+    t, d, x = tables.table(m.view(NP_BITS[dtype]))
+    rng = np.random.default_rng(T + 7 * D)
+    keep = rng.permutation(t.size)[: t.size - holes]
+    t, d, x = t[keep], d[keep], x[keep]
+    note(f"table_to_matrix binned {dtype} {T}x{D} holes={holes}")
+    got = csa.attn_table_to_matrix(torch.from_numpy(t).to(DEV), torch.from_numpy(d).to(DEV),
+                                   _to_dev(x, dtype), T, D)
+    torch.cuda.synchronize()
+    src = tables.matrix(t, d, np.arange(t.size, dtype=np.float64), T, D)
+    hole = np.isnan(src)
+    assert hole.sum() == holes
+    gb = _bits(got, dtype)
+    assert np.all(gb[hole] == NAN_BITS[dtype])
+    assert np.array_equal(gb[~hole], x[src[~hole].astype(np.int64)])
+
+
+@pytest.mark.parametrize("case,code", [("dup", 2), ("range", 1), ("both", 3), ("every row twice", 2)])
+def test_table_to_matrix_binned_status(case, code):
+    """The binned form's checks: a repeated cell (fewer marked cells than
+    counted rows), rows out of range, and more rows in range than cells (the
+    sorted rows would not fit: status 2 before the scatter)."""
+    import causal_softmax_attention_amd as csa
+    T, D = 256, 300
+    t, d, x = tables.table(np.arange(T * D, dtype=np.float32).reshape(T, D))
+    rng = np.random.default_rng(5)
+    if case == "every row twice":
+        t, d, x = (np.concatenate([a, a]) for a in (t, d, x))
+    p = rng.permutation(t.size)
+    t, d, x = t[p].copy(), d[p].copy(), x[p].copy()
+    if case in ("dup", "both"):
+        t[100], d[100] = t[60000], d[60000]
+    if case in ("range", "both"):
+        d[5] = -1
+        t[7000] = T
+    note(f"table_to_matrix binned status {case}")
+    _, status = csa.attn_table_to_matrix(*(torch.from_numpy(a).to(DEV) for a in (t, d, x)),
+                                         T, D, check=False)
+    torch.cuda.synchronize()
+    assert int(status.item()) == code
+
+
 def test_table_workload_round_trip():
     """The bench workload: a 524288 x 64 bfloat16 matrix (16 heads of 32768
     tokens), its 2^25 rows in a seeded random order, pivoted back.  The whole
