@@ -83,8 +83,10 @@ __device__ __forceinline__ bool all_finite_bf16x8(uint4 w) {
 }
 
 // Weights of one 64-key tile against the lane's reference max, packed to
-// bf16 pairs in B-operand order; returns the lane's sums of the rounded
-// weights per query column.
+// bf16 pairs in B-operand order; returns the lane's sums of the float32
+// weights per query column.  The sums use plain adds: a dot2 instruction
+// (bf16 pair times ones) does not issue while the matrix pipe is busy, so it
+// would hold this wave and the SIMD's other waves behind their MFMAs.
 __device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][kQT], float c_scale,
                                              const float (&mref)[kQT], uint32_t (&p)[kQT][2][8],
                                              float (&part)[kQT]) {
@@ -99,7 +101,7 @@ __device__ __forceinline__ void tile_weights(const floatx16 (&s)[2][kQT], float 
         const float a = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][2 * pr], c_scale, nm));
         const float b = __builtin_amdgcn_exp2f(fmaf(s[kt][qt][2 * pr + 1], c_scale, nm));
         p[qt][kt][pr] = pack_bf16(a, b);
-        acc = sum_bf16_pair(p[qt][kt][pr], acc);
+        acc += a + b;
       }
     part[qt] = acc;
   }
@@ -206,31 +208,32 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
       }
   } else {
     // ---- select path: a masked pair never multiplies (V holds inf/NaN).  The
-    // weights of one 32-query column and 16 keys go to the wave's LDS area as
+    // weights of one 32-query column and 8 keys go to the wave's LDS area as
     // [query][key].
 #pragma unroll
     for (int qt = 0; qt < kQT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int c16 = 0; c16 < 2; ++c16) {
+        for (int c8 = 0; c8 < 4; ++c8) {
 #pragma unroll
-          for (int pr = 4 * c16; pr < 4 * c16 + 4; ++pr) {
-            const int jj = acc_row(2 * pr, h) - 16 * c16;  // keys 32 kt + 16 c16 + jj, + 1
-            *(uint32_t*)(pscr + i32 * 16 + jj) = p[qt][kt][pr];
+          for (int pr = 2 * c8; pr < 2 * c8 + 2; ++pr) {
+            const int jj = acc_row(2 * pr, h) - 8 * c8;  // keys 32 kt + 8 c8 + jj, + 1
+            *(uint32_t*)(pscr + i32 * 8 + jj) = p[qt][kt][pr];
           }
           __builtin_amdgcn_wave_barrier();
           const int qi = qw + 32 * qt + i32;
-          for (int jj = 0; jj < 16; ++jj) {
-            const int j = k0 + 32 * kt + 16 * c16 + jj;
-            const float pj = (float)pscr[i32 * 16 + jj];
+#pragma unroll 1
+          for (int jj = 0; jj < 8; ++jj) {
+            const int j = k0 + 32 * kt + 8 * c8 + jj;
+            const float pj = (float)pscr[i32 * 8 + jj];
             if (absent(qi, j, N, causal, band) || (SEG && segk[j - k0] != sq)) continue;
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
               for (int r2 = 0; r2 < 16; ++r2)
                 oacc[dt][qt][r2] +=
-                    pj * (float)vs[lds_at(32 * kt + 16 * c16 + jj, 32 * dt + acc_row(r2, h))];
+                    pj * (float)vs[lds_at(32 * kt + 8 * c8 + jj, 32 * dt + acc_row(r2, h))];
           }
           __builtin_amdgcn_wave_barrier();
         }
@@ -248,7 +251,9 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
   __shared__ KVStage st0, st1, st2;
-  __shared__ __bf16 pscr[kWaves][32 * 16];
+  // the select path's weights (32 queries x 8 keys a wave): at 32 x 16 the
+  // segment variant's LDS (with its key ids) kept only 2 workgroups on a CU
+  __shared__ __bf16 pscr[kWaves][32 * 8];
   __shared__ __attribute__((aligned(16))) int32_t sg[3][SEG ? kBc : 4];  // the stages' key ids
   static_assert(kQT == 1, "one query column per wave");
   int head, qb;
