@@ -73,13 +73,16 @@ struct KVStage {
   __bf16 v[kBc * kD];
 };
 
-__device__ __forceinline__ bool all_finite_bf16x8(uint4 w) {
-  // a bf16 value is non-finite when its 8 exponent bits are all ones
-  auto bad = [](uint32_t x) {
-    const uint32_t e = x & 0x7f807f80u;
-    return (int)((e & 0xffffu) == 0x7f80u) | (int)((e >> 16) == 0x7f80u);
-  };
-  return (bad(w.x) | bad(w.y) | bad(w.z) | bad(w.w)) == 0;
+// Running maximum, per 16-bit half, of the magnitude bits (sign cleared) of
+// bf16 pairs: a bf16 value is non-finite exactly when its magnitude bits reach
+// 0x7f80 (all exponent bits set), so one compare of the maximum at the end
+// tests every value (two instructions per word: an and, a packed max).
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2_t max_mag_bf16x8(u16x2_t acc, uint4 w) {
+  acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2_t, w.x & 0x7fff7fffu));
+  acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2_t, w.y & 0x7fff7fffu));
+  acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2_t, w.z & 0x7fff7fffu));
+  return __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2_t, w.w & 0x7fff7fffu));
 }
 
 // Weights of one 64-key tile against the lane's reference max, packed to
@@ -147,10 +150,15 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
             sk[4 * g + 0] = w.x; sk[4 * g + 1] = w.y; sk[4 * g + 2] = w.z; sk[4 * g + 3] = w.w;
           }
         }
+        // register r holds key j = jb + acc_row(r, 0), so the predicate of
+        // absent() becomes a range of that constant offset: lo < off < hi
+        const int jb = k0 + 32 * kt + 4 * h;
+        const int hi = causal ? min(N, qi + 1) - jb : N - jb;
+        const int lo = band ? qi - band - jb : INT32_MIN;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int j = k0 + 32 * kt + acc_row(r, h);
-          const bool gone = absent(qi, j, N, causal, band) || (SEG && sk[r] != sq);
+          const int off = acc_row(r, 0);
+          const bool gone = !(off < hi && off > lo) || (SEG && sk[r] != sq);
           s[kt][qt][r] = gone ? -__builtin_inff() : s[kt][qt][r];
         }
       }
@@ -190,10 +198,10 @@ __device__ __forceinline__ void fwd_tile(const __bf16* ks, const __bf16* vs, __b
   bool vbad = false;
   if (MASKED) {
     // lane l scans row l of the V tile for inf / NaN
-    int bad = 0;
+    u16x2_t mag = {0, 0};
 #pragma unroll
-    for (int c = 0; c < 8; ++c) bad |= !all_finite_bf16x8(*(const uint4*)(vs + lane * kD + 8 * c));
-    vbad = __any(bad);
+    for (int c = 0; c < 8; ++c) mag = max_mag_bf16x8(mag, *(const uint4*)(vs + lane * kD + 8 * c));
+    vbad = __any(mag.x >= 0x7f80u || mag.y >= 0x7f80u);
   }
   if (!vbad) {
     // ---- O^T += V^T P^T over 4 chunks of 16 keys
@@ -250,7 +258,11 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
     const int32_t* __restrict__ seg, int hpb) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
-  __shared__ KVStage st0, st1, st2;
+  // one array, so the three stages' LDS addresses differ by immediate offsets
+  // and share their per-lane address registers (separate objects took one
+  // set per stage: 16 more VGPRs, and spills in the masked variants)
+  __shared__ KVStage stg[3];
+  KVStage &st0 = stg[0], &st1 = stg[1], &st2 = stg[2];
   // the select path's weights (32 queries x 8 keys a wave): at 32 x 16 the
   // segment variant's LDS (with its key ids) kept only 2 workgroups on a CU
   __shared__ __bf16 pscr[kWaves][32 * 8];
