@@ -176,6 +176,12 @@ __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[kKT], const flo
 #pragma unroll
   for (int kt = 0; kt < kKT; ++kt) {
     const int key = kw + 32 * kt + i32;
+    // register r holds query qb + acc_row(r, 0): the pair is present when that
+    // offset is at least lo (causal: query >= key) and below hi (window:
+    // query - key < band)
+    const int qb = qrow0 + 4 * h;
+    const int lo = causal ? key - qb : INT32_MIN;
+    const int hi = band ? key + band - qb : INT32_MAX;
 #pragma unroll
     for (int pr = 0; pr < 8; ++pr) {
       float pv[2], dsv[2];
@@ -184,9 +190,8 @@ __device__ __forceinline__ void dkdv_softmax(const floatx16 (&s)[kKT], const flo
         const int r = 2 * pr + e;
         float p = __builtin_amdgcn_exp2f(s[kt][r] * c_scale);
         if (MASKED) {
-          const int qi = qrow0 + acc_row(r, h);
-          p = (causal && key > qi) || (band && qi - key >= band) || (SEG && qs[r] != sk) ? 0.f
-                                                                                          : p;
+          const int off = acc_row(r, 0);
+          p = !(off >= lo && off < hi) || (SEG && qs[r] != sk) ? 0.f : p;
         }
         pv[e] = p;
         dsv[e] = p * dp[kt][r];

@@ -68,6 +68,47 @@ __device__ __forceinline__ void dq_half_softmax(const floatx16 (&s)[kQT], const 
   }
 }
 
+// dq_half_softmax of a masked tile in the window and segment kernels, with
+// the predicate tested as a range of each register's key offset: register r
+// holds key kb + acc_row(r, 0), present when that offset lies strictly
+// between lo and hi (fewer instructions per tile; the causal and full
+// kernels keep the form above, which compiled to their faster loops).
+template <bool SEG>
+__device__ __forceinline__ void dq_half_softmax_range(const floatx16 (&s)[kQT],
+                                                      const floatx16 (&dp)[kQT],
+                                                      uint32_t (&dsp)[kQT][8], int kt, int k0,
+                                                      int qw, int N, int i32, int h,
+                                                      float c_scale, int causal, int band,
+                                                      const int32_t* segk, int32_t sq) {
+  int32_t sk[16];  // ids of the lane's 16 keys of this half
+  if (SEG) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int4 w = *(const int4*)(segk + 32 * kt + 8 * g + 4 * h);
+      sk[4 * g + 0] = w.x; sk[4 * g + 1] = w.y; sk[4 * g + 2] = w.z; sk[4 * g + 3] = w.w;
+    }
+  }
+#pragma unroll
+  for (int qt = 0; qt < kQT; ++qt) {
+    const int qi = qw + 32 * qt + i32;
+    const int kb = k0 + 32 * kt + 4 * h;
+    const int hi = causal ? min(N, qi + 1) - kb : N - kb;
+    const int lo = band ? qi - band - kb : INT32_MIN;
+#pragma unroll
+    for (int pr = 0; pr < 8; ++pr) {
+      float dsv[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 2 * pr + e;
+        const int off = acc_row(r, 0);
+        const float p = __builtin_amdgcn_exp2f(s[qt][r] * c_scale);
+        dsv[e] = (!(off < hi && off > lo) || (SEG && sk[r] != sq) ? 0.f : p) * dp[qt][r];
+      }
+      dsp[qt][pr] = pack_bf16(dsv[0], dsv[1]);
+    }
+  }
+}
+
 __device__ __forceinline__ void dq_half_scores(const __bf16* ks, const __bf16* vs, int kt,
                                                int i32, int h, const bf16x8_t (&qop)[kQT][4],
                                                const bf16x8_t (&oop)[kQT][4],
@@ -97,7 +138,7 @@ __device__ __forceinline__ void dq_half_scores(const __bf16* ks, const __bf16* v
   }
 }
 
-template <bool MASKED, bool SEG>
+template <bool MASKED, bool SEG, bool RANGE = false>
 __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int lane, int k0,
                                         int qw, int N, float c_scale,
                                         const bf16x8_t (&qop)[kQT][4], const bf16x8_t (&oop)[kQT][4],
@@ -114,8 +155,12 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
     for (int dt = 0; dt < 2; ++dt) ktr0[half][dt] = read_tr(ks, lane, half, 32 * dt);
   dq_half_scores(ks, vs, 1, i32, h, qop, oop, nls, ndl, s1, dp1);
-  dq_half_softmax<MASKED, SEG>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale, causal, band,
-                               segk, sq);
+  if constexpr (MASKED && RANGE)
+    dq_half_softmax_range<SEG>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale, causal, band, segk,
+                               sq);
+  else
+    dq_half_softmax<MASKED, SEG>(s0, dp0, dsp0, 0, k0, qw, N, i32, h, c_scale, causal, band,
+                                 segk, sq);
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -127,8 +172,12 @@ __device__ __forceinline__ void dq_tile(const __bf16* ks, const __bf16* vs, int 
 #pragma unroll
       for (int qt = 0; qt < kQT; ++qt)
         dqacc[dt][qt] = mma(ktr0[half][dt], chunk_op(dsp0[qt], half), dqacc[dt][qt]);
-  dq_half_softmax<MASKED, SEG>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale, causal, band,
-                               segk, sq);
+  if constexpr (MASKED && RANGE)
+    dq_half_softmax_range<SEG>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale, causal, band, segk,
+                               sq);
+  else
+    dq_half_softmax<MASKED, SEG>(s1, dp1, dsp1, 1, k0, qw, N, i32, h, c_scale, causal, band,
+                                 segk, sq);
 #pragma unroll
   for (int half = 0; half < 2; ++half)
 #pragma unroll
@@ -248,8 +297,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
         // masked: some pair of the tile is absent for some query of the wave
         if ((causal && k0 + kT - 1 > qw) || (k0 + kT > N) || (band && k0 < qw + kRowsW - band) ||
             !seg_one)
-          dq_tile<true, SEG>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc,
-                             causal, band, sgc, sq);
+          dq_tile<true, SEG, SEG || BANDED>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, nls,
+                                            ndl, dqacc, causal, band, sgc, sq);
         else
           dq_tile<false, SEG>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc,
                               causal, band, sgc, sq);
