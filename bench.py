@@ -502,6 +502,9 @@ def main():
     ap.add_argument("--steps-before-only", action="store_true",
                     help="time only the Q/K/V projection and the long-table adapter (one JSON "
                          "line of those); for profiling their kernels")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock-sampling steps after the timed ones (no amdsmi thread; "
+                         "for rocprofv3 counter runs, which need only the kernels' dispatches)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy (3x), the known-size check "
                          "of the byte counts derived from rocprofv3 request counters")
@@ -546,14 +549,18 @@ def main():
     # the GPU's clock readings refresh more slowly than the ~55 ms timed region,
     # so the clock is sampled over about 2.5 s of the same step right after it,
     # with every kernel timed (the per-kernel breakdown of the record)
-    sustain = max(50, int(2500.0 / ms))
-    log(f"sampling the graphics clock over {sustain} more steps")
-    with SclkSampler(period_s=0.01) as clk:
-        sus_ms, _, sus_per, _, _ = time_attention(q, k, v, sustain, 0)
-    sclk = clk.summary()
-    sclk["window"] = (f"{sustain} steps of the same fwd+bwd ({sustain * sus_ms / 1e3:.2f} s) "
-                      "run right after the timed steps, every kernel timed")
-    sclk["ms_per_step_over_window"] = round(sus_ms, 4)
+    if args.no_clock:
+        sclk = {"skipped": "--no-clock"}
+        sus_per = per
+    else:
+        sustain = max(50, int(2500.0 / ms))
+        log(f"sampling the graphics clock over {sustain} more steps")
+        with SclkSampler(period_s=0.01) as clk:
+            sus_ms, _, sus_per, _, _ = time_attention(q, k, v, sustain, 0)
+        sclk = clk.summary()
+        sclk["window"] = (f"{sustain} steps of the same fwd+bwd ({sustain * sus_ms / 1e3:.2f} s) "
+                          "run right after the timed steps, every kernel timed")
+        sclk["ms_per_step_over_window"] = round(sus_ms, 4)
     flops = 14 * D * pairs(B * H, N)
     value = flops / ms / 1e9
     kflops = algo[dom] * pairs(B * H, N)
