@@ -240,6 +240,9 @@ __device__ __forceinline__ void dkdv_step(const QStageT<SEG>& sa, int ra, const 
   for (int kt = 0; kt < kKT; ++kt)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      // empty asm on B's results: they are formed inside this step, so every
+      // step carries its own softmax work beside its MFMAs
+      asm volatile("" : "+v"(pp[kt][i]), "+v"(dsp[kt][i]));
       pipe.pp[kt][i] = pp[kt][i];
       pipe.dsp[kt][i] = dsp[kt][i];
     }
