@@ -225,6 +225,42 @@ def test_inf_value_several_tiles(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("mask,window", [(None, 0), ("full", 0), ("window", 300)],
+                         ids=lambda x: str(x))
+def test_negative_inf_and_nan_values(dtype, mask, window):
+    """V[150, 3] = -inf and V[400, 7] = NaN in one head of 700 tokens: each reaches
+    exactly the rows whose pairs include its key (causal: rows >= j; full: every
+    row; a 300-key window: rows j .. j + 299), in its own column only, so the
+    masked tiles' scan for non-finite V must catch both kinds."""
+    B, H, N = 1, 1, 700
+    a = inp.attention_inputs(77, B, H, N, dtype)
+    note(f"-inf and NaN in V, {mask} {window} {dtype}")
+    q, k, v = (to_dev(getattr(a, x), dtype) for x in "qkv")
+    v[0, 0, 150, 3] = float("-inf")
+    v[0, 0, 400, 7] = float("nan")
+    vh = a.as_f64("v")[0, 0].copy()
+    vh[150, 3] = -np.inf
+    vh[400, 7] = np.nan
+    o, lse = run_fwd(q, k, v, S, mask=mask, window=window)
+    oh, lh = to_host(o)[0, 0], to_host(lse)[0, 0]
+    rows = np.arange(N)
+    for j, c in ((150, 3), (400, 7)):
+        if mask == "full":
+            hit = np.ones(N, bool)
+        elif mask == "window":
+            hit = (rows >= j) & (rows - j < window)
+        else:
+            hit = rows >= j
+        assert (~np.isfinite(oh[hit, c])).all() and np.isfinite(oh[~hit, c]).all()
+    assert np.isfinite(np.delete(oh, [3, 7], axis=1)).all() and np.isfinite(lh).all()
+    omode = mask or "causal"
+    wo, wl = oracle.forward_head(a.as_f64("q")[0, 0], a.as_f64("k")[0, 0], vh, S, mask=omode,
+                                 window=window)[:2]
+    assert_close("o (-inf / NaN run)", oh, wo, TOL[dtype])
+    assert_close("lse (-inf / NaN run)", lh, wl, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_page_mask_case(dtype):
     """The demo's own mask check: n = 16, +inf at v[9, 0], seed 1."""
     q, k, v, j = inp.page_mask_inputs()
