@@ -76,11 +76,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, p);
 }
 
-__device__ __forceinline__ float sum_bf16_pair(uint32_t p, float acc) {
-  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, p), one, acc, false);
-}
-
 // B operand of chunk c (rows 16c..16c+15 of a 32-row tile: c in {0,1}) from a
 // bf16-packed accumulator tile held as 8 dwords.
 __device__ __forceinline__ bf16x8_t chunk_op(const uint32_t* packed8, int c) {
