@@ -63,22 +63,34 @@ __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ 
                                                      float* __restrict__ ndelta,
                                                      float* __restrict__ nlse, float inv_scale,
                                                      int64_t rows) {
-  const int64_t r = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  // 128 rows per workgroup: each thread has 4 rows' loads in flight
   const int part = threadIdx.x & 7;
-  float s = 0.f;
-  if (r < rows) {
-    const uint4 a = ldg16(o + r * kD + part * 8), b = ldg16(dout + r * kD + part * 8);
-    const __bf16* x = (const __bf16*)&a;
-    const __bf16* y = (const __bf16*)&b;
+  const int64_t r0 = (int64_t)blockIdx.x * 128 + (threadIdx.x >> 3);
+  uint4 a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + 32 * i;
+    a[i] = b[i] = make_uint4(0, 0, 0, 0);
+    if (r < rows) {
+      a[i] = ldg16(o + r * kD + part * 8);
+      b[i] = ldg16(dout + r * kD + part * 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = r0 + 32 * i;
+    const __bf16* x = (const __bf16*)&a[i];
+    const __bf16* y = (const __bf16*)&b[i];
+    float s = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
-  }
-  s += __shfl_xor(s, 1);
-  s += __shfl_xor(s, 2);
-  s += __shfl_xor(s, 4);
-  if (r < rows && part == 0) {
-    ndelta[r] = -s;
-    nlse[r] = -lse[r] * inv_scale;
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (r < rows && part == 0) {
+      ndelta[r] = -s;
+      nlse[r] = -lse[r] * inv_scale;
+    }
   }
 }
 
@@ -437,7 +449,7 @@ hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, co
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nb);
   if (!prepared) {  // else the forward already wrote both per-row values (dO = O)
     if (hipError_t e = mark(tm.start[kTimerBwdPre], stream)) return e;
-    hipLaunchKernelGGL(bwd_prep_bf16, dim3((unsigned)((rows + 31) / 32)), dim3(256), 0, stream, o,
+    hipLaunchKernelGGL(bwd_prep_bf16, dim3((unsigned)((rows + 127) / 128)), dim3(256), 0, stream, o,
                        dout, lse, ndelta, nlse, (float)(1.0 / scale), rows);
     if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
   }
