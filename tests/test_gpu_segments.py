@@ -81,21 +81,34 @@ def test_seg_fwd_bwd(kind, dtype, mask, window, shape):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("mask,window", MASKS, ids=lambda x: str(x))
-def test_one_segment_is_no_segment(dtype, mask, window):
+@pytest.mark.parametrize("shape", [(1, 2, 333), (2, 3, 1000), (2, 3, 1024), (1, 2, 4096)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_one_segment_is_no_segment(dtype, mask, window, shape):
     """Every token in one segment (id 7): the segment entry points give the
-    results of attn_fwd / attn_bwd under the same mask, bit for bit (equal ids
-    only keep weights; no arithmetic changes)."""
-    B, H, N = 1, 2, 333
+    results of attn_fwd / attn_bwd under the same mask (equal ids only keep
+    weights).  Bit for bit when N fills whole query blocks (256 rows); with a
+    ragged last block the padding rows past N see no key in the segment
+    kernels (their id is none of the keys') but some keys in the plain ones,
+    and a lane's vote for the wave's shared exact-max step can then differ, so
+    there the two agree to the tolerance.  For the bf16 causal forward the
+    bit-for-bit cases also pin the loop that carries each plain tile's P V into
+    the next tile's step (the segment kernel runs the plain loop)."""
+    B, H, N = shape
+    exact = N % 256 == 0
     a = inp.attention_inputs(91, B, H, N, dtype)
-    note(f"one segment {mask} {window} {dtype}")
+    note(f"one segment {mask} {window} {dtype} {shape}")
     q, k, v = (to_dev(getattr(a, x), dtype) for x in "qkv")
     sd = _seg_dev(np.full((B, N), 7))
     o1, l1 = run_fwd(q, k, v, S, mask=mask, window=window)
     o2, l2 = run_fwd(q, k, v, S, mask=mask, window=window, seg=sd)
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
     g1 = run_bwd(q, k, v, o1, o1, l1, S, mask=mask, window=window)
     g2 = run_bwd(q, k, v, o1, o1, l1, S, mask=mask, window=window, seg=sd)
-    assert all(torch.equal(x, y) for x, y in zip(g1, g2))
+    pairs = [("o", o1, o2), ("lse", l1, l2)] + [(n, x, y) for n, x, y in zip(("dq", "dk", "dv"), g1, g2)]
+    for name, x, y in pairs:
+        if exact:
+            assert torch.equal(x, y), name
+        else:
+            assert_close(name, to_host(y), to_host(x), TOL[dtype])
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
