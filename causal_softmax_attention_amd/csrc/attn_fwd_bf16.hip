@@ -21,7 +21,9 @@
 //     lost.)
 //   * Keys stream in tiles of 64 through a 3-stage LDS ring, filled by
 //     asynchronous bounds-checked buffer loads two tiles ahead (one barrier per
-//     tile).  K rows feed the A operand with plain 16-byte reads; V rows are
+//     tile; one tile ahead in the plain causal kernel, which runs each plain
+//     tile's P V in the next tile's step and keeps that V in the third stage).
+//     K rows feed the A operand with plain 16-byte reads; V rows are
 //     read with ds_read_b64_tr_b16, which hands each lane 4 consecutive keys of
 //     one feature column: exactly the A operand of O^T = V^T P^T.  The
 //     bf16-rounded P accumulator registers are the B operand as they stand.
