@@ -330,12 +330,14 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) int32_t sg[3][SEG ? kBc : 4];  // the stages' key ids
   static_assert(kQT == 1, "one query column per wave");
   int head, qb;
-  // groups of 3 heads: an XCD holds 96 of these workgroups at once (32 CUs x
-  // 3), about one group, whose K/V (3 x 1 MiB at N = 4096) fits its 4 MiB L2.
-  // Measured at that size: with groups of 8 the forward read 2.6 times its Q,
-  // K and V bytes from beyond L2, with groups of 3 1.26 times, in the same
-  // time within run-to-run noise.
-  if (!map_block(blockIdx.x, heads, nqb, true, 3, head, qb)) return;
+  // groups of 4 heads: an XCD holds 96 of these workgroups at once (32 CUs x
+  // 3), a little under one group, whose K/V (4 x 1 MiB at N = 4096) about
+  // fills its 4 MiB L2.  Measured at that size: groups of 8 read 2.6 times the
+  // forward's Q, K and V bytes from beyond L2, groups of 4 1.5 times and groups
+  // of 3 1.26 times; timed in alternating rounds, groups of 4 and 8 ran 3 %
+  // faster than groups of 3, whose last group's heaviest blocks start late and
+  // leave the launch a tail.
+  if (!map_block(blockIdx.x, heads, nqb, true, 4, head, qb)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i32 = lane & 31, h = lane >> 5;
   const size_t base = (size_t)head * N * kD;
