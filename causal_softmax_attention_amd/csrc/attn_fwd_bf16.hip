@@ -282,8 +282,11 @@ __device__ __forceinline__ void fwd_tile_defer(const __bf16* ks, const __bf16* v
   if (PEND) pv_mfma(vprev, lane, pprev, oacc);
   uint32_t p[kQT][2][8];
   float part[kQT];
-  tile_weights(s, c_scale, mref, p, part);
-  if (__any(!(part[0] <= kTau))) {
+  // with nothing pending this is the wave's first tile (its plain tiles come
+  // before every masked one), whose reference is still kRefInit: it takes the
+  // exact max at once instead of after a lazy attempt that must overflow
+  if (PEND) tile_weights(s, c_scale, mref, p, part);
+  if (!PEND || __any(!(part[0] <= kTau))) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 3) void attn_fwd_bf16_kernel(
   // of 3 1.26 times; timed in alternating rounds, groups of 4 and 8 ran 3 %
   // faster than groups of 3, whose last group's heaviest blocks start late and
   // leave the launch a tail.
-  if (!map_block(blockIdx.x, heads, nqb, true, 4, head, qb)) return;
+  if (!map_block(blockIdx.x, heads, nqb, true, 4, head, qb, true)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i32 = lane & 31, h = lane >> 5;
   const size_t base = (size_t)head * N * kD;

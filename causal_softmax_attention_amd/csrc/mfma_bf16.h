@@ -94,15 +94,27 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 // then rank 1, ...), where rank r is block nblk - 1 - r when `last_first` (the
 // causal forward and dQ, whose last block walks the most keys) and block r
 // otherwise.  Under a causal mask the light blocks then fill the end of the
-// launch instead of one head's heavy block starting last.
+// launch instead of one head's heavy block starting last.  With merge_tail,
+// the last two whole groups and any remainder form one final group: a final
+// group of few heads holds few blocks per slot of the XCD, so its heaviest
+// blocks, starting near the end of the launch, would leave a tail.
 __device__ __forceinline__ bool map_block(int b, int heads, int nblk, bool last_first, int group,
-                                          int& head, int& blk) {
+                                          int& head, int& blk, bool merge_tail = false) {
   const int xcd = b & 7, slot = b >> 3;
   const int hx = (heads - xcd + 7) >> 3;  // heads with head % 8 == xcd
   if (slot >= hx * nblk) return false;
-  const int chunk = slot / (group * nblk), within = slot - chunk * group * nblk;
-  const int h0 = chunk * group;
-  const int gc = min(group, hx - h0);     // heads in this group (the last may be short)
+  const int tail0 = merge_tail ? max(0, (hx / group - 2) * group) : hx;  // first head of the final group
+  int h0, gc, within;
+  if (slot >= tail0 * nblk) {
+    h0 = tail0;
+    gc = hx - tail0;
+    within = slot - tail0 * nblk;
+  } else {
+    const int chunk = slot / (group * nblk);
+    h0 = chunk * group;
+    gc = min(group, hx - h0);             // heads in this group (the last may be short)
+    within = slot - chunk * group * nblk;
+  }
   const int r = within / gc, hi = h0 + within % gc;
   head = xcd + 8 * hi;
   blk = last_first ? nblk - 1 - r : r;
