@@ -98,9 +98,11 @@ def _check_all_heads(a, o, lse, grads, tol):
 
 def _grid_heads(B, H):
     """Flat heads covering every XCD (workgroup b runs on XCD b % 8 and takes
-    heads b % 8, b % 8 + 8, ...) and every position in the forward's groups of
-    8 and the backward's groups of 4 heads per XCD: head x + 8 x (first group,
-    position x) and head x + 8 (n - 1 - x) (last group), as (b, h)."""
+    heads b % 8, b % 8 + 8, ...) and the first and last 8 heads of each XCD's
+    sequence, so every position in its first and last groups (groups of 4
+    heads in the forward, whose last two form one group of 8, and in the
+    backward): head x + 8 x (the XCD's head x) and head x + 8 (n - 1 - x)
+    (its head n - 1 - x), as (b, h)."""
     n = (B * H) // 8
     flat = sorted({x + 8 * min(x, n - 1) for x in range(8)} |
                   {x + 8 * max(n - 1 - x, 0) for x in range(8)})
