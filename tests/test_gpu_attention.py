@@ -165,6 +165,21 @@ def test_head_groups(dtype):
     _check_bwd(a, grads)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_merged_last_group(dtype):
+    """100 heads: 12 or 13 per XCD, so the bf16 forward's groups of 4 heads
+    end in one merged group of 8 or 9 after a whole group of 4.  Every (head,
+    block) must be computed exactly once: all heads against the oracle."""
+    B, H, N = 4, 25, 200
+    a = inp.attention_inputs(22, B, H, N, dtype)
+    note(f"merged last head group fwd+bwd {dtype} B={B} H={H} N={N}")
+    q, k, v = (to_dev(getattr(a, x), dtype) for x in "qkv")
+    o, lse = run_fwd(q, k, v, S)
+    _check_fwd(a, o, lse)
+    grads = run_bwd(q, k, v, o, o, lse, S)
+    _check_bwd(a, grads)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_general_dout(dtype):
     """An upstream gradient that is not o (same seeded dout on both sides)."""
