@@ -19,7 +19,7 @@ constexpr int kQT = 1;                   // 32-query MFMA columns per wave
 constexpr int kRowsW = 32 * kQT;         // queries per wave
 constexpr int kBlk = kRowsW * kWaves;    // queries per workgroup
 constexpr int kT = 64;                   // keys per tile
-constexpr int kT2 = kT;                  // keys per LDS stage
+constexpr int kT2 = 2 * kT;              // keys per LDS stage (two tiles: one barrier per 48 MFMAs)
 
 // ---- dQ, query-stationary ---------------------------------------------------
 //
@@ -202,9 +202,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
     float c_scale, float scale, int band_arg, const int32_t* __restrict__ seg, int hpb) {
   constexpr int causal = CAUSAL;
   const int band = BANDED ? band_arg : 0;
-  __shared__ KVStage st0, st1, st2;
-  __shared__ __attribute__((aligned(16))) int32_t sg[3][SEG ? kT2 : 4];  // the stages' key ids
-  static_assert(kQT == 1 && kT2 == kT, "one query column per wave, one tile per stage");
+  __shared__ KVStage st0, st1;
+  __shared__ __attribute__((aligned(16))) int32_t sg[2][SEG ? kT2 : 4];  // the stages' key ids
+  static_assert(kQT == 1 && kT2 == 2 * kT, "one query column per wave, two tiles per stage");
   int head, qb;
   if (!map_block(blockIdx.x, heads, nqb, true, 4, head, qb)) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -272,17 +272,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
   const __amdgpu_buffer_rsrc_t rk = head_rsrc(k + base, tbytes), rv = head_rsrc(v + base, tbytes);
   __amdgpu_buffer_rsrc_t rs = rk;
   if (SEG) rs = head_rsrc(segrow, (uint32_t)N * 4);
-  // wave 0 also copies the tile's key ids (one more load per tile; the barrier
-  // waits still leave only the newest tile's loads in flight)
+  // wave 0 also copies the stage's key ids (two more loads per stage)
   auto issue = [&](KVStage& s, int32_t* sgs, int t) {
     tile_async<kT2, kWaves>(rk, s.k, t * kT2, wave, lane);
     tile_async<kT2, kWaves>(rv, s.v, t * kT2, wave, lane);
-    if (SEG && wave == 0) rows_async(rs, (float*)sgs, t * kT2, lane);
+    if (SEG && wave == 0) {
+      rows_async(rs, (float*)sgs, t * kT2, lane);
+      rows_async(rs, (float*)sgs + kT, t * kT2 + kT, lane);
+    }
   };
-  auto step = [&](KVStage& cur, int32_t* sgc, KVStage& ahead, int32_t* sga, int t) {
-    const bool pre = t + 2 < ntiles;
-    if (pre) issue(ahead, sga, t + 2);
-    const int k0 = t * kT2;
+  // one 64-key tile of a stage (keys k0 .. k0 + 63, at ks / vs / sgc in LDS)
+  auto tile = [&](const __bf16* ks, const __bf16* vs, const int32_t* sgc,
+                  int k0) __attribute__((always_inline)) {
     if (k0 <= whi && k0 + kT - 1 >= wlo) {
       // segments: no key id in the wave's id range -> no pair; all ids one and
       // the same -> the ids mask nothing
@@ -297,24 +298,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16(
         // masked: some pair of the tile is absent for some query of the wave
         if ((causal && k0 + kT - 1 > qw) || (k0 + kT > N) || (band && k0 < qw + kRowsW - band) ||
             !seg_one)
-          dq_tile<true, SEG, SEG || BANDED>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, nls,
-                                            ndl, dqacc, causal, band, sgc, sq);
+          dq_tile<true, SEG, SEG || BANDED>(ks, vs, lane, k0, qw, N, c_scale, qop, oop, nls, ndl,
+                                            dqacc, causal, band, sgc, sq);
         else
-          dq_tile<false, SEG>(cur.k, cur.v, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc,
-                              causal, band, sgc, sq);
+          dq_tile<false, SEG>(ks, vs, lane, k0, qw, N, c_scale, qop, oop, nls, ndl, dqacc, causal,
+                              band, sgc, sq);
       }
     }
-    if (pre) wait_vm_barrier<2 * kT2 / (8 * kWaves)>();
-    else wait_vm_barrier<0>();
+  };
+  // a two-stage ring: stage t + 1 is issued into the buffer that stage t - 1
+  // left (every wave passed the barrier after it) and has all of stage t's
+  // two tiles to land
+  auto step = [&](KVStage& cur, int32_t* sgc, KVStage& ahead, int32_t* sga, int t) {
+    if (t + 1 < ntiles) issue(ahead, sga, t + 1);
+    tile(cur.k, cur.v, sgc, t * kT2);
+    tile(cur.k + kT * kD, cur.v + kT * kD, sgc + kT, t * kT2 + kT);
+    wait_vm_barrier<0>();  // stage t + 1 has landed; every wave is done with stage t
   };
 
   issue(st0, sg[0], t0);
-  if (t0 + 1 < ntiles) issue(st1, sg[1], t0 + 1);
   wait_vm_barrier<0>();
-  for (int t = t0; t < ntiles; t += 3) {
-    step(st0, sg[0], st2, sg[2], t);
+  for (int t = t0; t < ntiles; t += 2) {
+    step(st0, sg[0], st1, sg[1], t);
     if (t + 1 < ntiles) step(st1, sg[1], st0, sg[0], t + 1);
-    if (t + 2 < ntiles) step(st2, sg[2], st1, sg[1], t + 2);
   }
 
 #pragma unroll
