@@ -56,31 +56,36 @@ constexpr int kT2 = kT;                  // streamed rows per LDS stage
 // Per row: -delta_i = -sum_d dO_id O_id and -lse_i / scale, the values the
 // score accumulators of both passes start from (so that they end as
 // dP_ij - delta_i and s_ij - lse_i / scale, see below).  Eight lanes per row,
-// 16 bytes each.
+// 16 bytes each.  ALIAS: dO is O (one pointer, as for the loss sum(o^2)/2), so
+// each row is read once and delta_i = |o_i|^2 (the same products in the same
+// order as the general form).
+template <bool ALIAS>
 __global__ __launch_bounds__(256) void bwd_prep_bf16(const __bf16* __restrict__ o,
                                                      const __bf16* __restrict__ dout,
                                                      const float* __restrict__ lse,
                                                      float* __restrict__ ndelta,
                                                      float* __restrict__ nlse, float inv_scale,
                                                      int64_t rows) {
-  // 128 rows per workgroup: each thread has 4 rows' loads in flight
+  // 32 R rows per workgroup: each thread has R rows' loads in flight (the
+  // same bytes either way)
+  constexpr int R = ALIAS ? 8 : 4;
   const int part = threadIdx.x & 7;
-  const int64_t r0 = (int64_t)blockIdx.x * 128 + (threadIdx.x >> 3);
-  uint4 a[4], b[4];
+  const int64_t r0 = (int64_t)blockIdx.x * (32 * R) + (threadIdx.x >> 3);
+  uint4 a[R], b[R];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < R; ++i) {
     const int64_t r = r0 + 32 * i;
     a[i] = b[i] = make_uint4(0, 0, 0, 0);
     if (r < rows) {
       a[i] = ldg16(o + r * kD + part * 8);
-      b[i] = ldg16(dout + r * kD + part * 8);
+      if (!ALIAS) b[i] = ldg16(dout + r * kD + part * 8);
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < R; ++i) {
     const int64_t r = r0 + 32 * i;
     const __bf16* x = (const __bf16*)&a[i];
-    const __bf16* y = (const __bf16*)&b[i];
+    const __bf16* y = ALIAS ? x : (const __bf16*)&b[i];
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) s = fmaf((float)x[e], (float)y[e], s);
@@ -449,8 +454,12 @@ hipError_t launch_bwd_bf16(const __bf16* q, const __bf16* k, const __bf16* v, co
   const unsigned grid = (unsigned)(8 * ((heads + 7) / 8) * nb);
   if (!prepared) {  // else the forward already wrote both per-row values (dO = O)
     if (hipError_t e = mark(tm.start[kTimerBwdPre], stream)) return e;
-    hipLaunchKernelGGL(bwd_prep_bf16, dim3((unsigned)((rows + 127) / 128)), dim3(256), 0, stream, o,
-                       dout, lse, ndelta, nlse, (float)(1.0 / scale), rows);
+    if (dout == o)
+      hipLaunchKernelGGL(bwd_prep_bf16<true>, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0,
+                         stream, o, dout, lse, ndelta, nlse, (float)(1.0 / scale), rows);
+    else
+      hipLaunchKernelGGL(bwd_prep_bf16<false>, dim3((unsigned)((rows + 127) / 128)), dim3(256), 0,
+                         stream, o, dout, lse, ndelta, nlse, (float)(1.0 / scale), rows);
     if (hipError_t e = mark(tm.stop[kTimerBwdPre], stream)) return e;
   }
   if (hipError_t e = mark(tm.start[kTimerBwdDkdv], stream)) return e;
